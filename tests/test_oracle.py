@@ -1,0 +1,340 @@
+"""Pins of the fp64 oracle against things other than itself.
+
+Each test ties the oracle to a fact the pages or the mathematics fix:
+  * a hand-derived worked example (tests/golden/worked_tree_example.json);
+  * brute force (explicit key lists walked from the parent array, pure-Python
+    fsum arithmetic) on every topologically ordered tree with N <= 5;
+  * chain-shaped tree == causal attention, via torch's scaled_dot_product_attention
+    in fp64 with an explicit bottom-right mask;
+  * q = 0 closed form (uniform weights over the visible set);
+  * L = 0, N = 1 closed form (out = V[root]);
+  * planted keys (a dominant visible key wins; a dominant hidden sibling does not);
+  * split + merge == unsplit over arbitrary key partitions;
+  * slot-permutation invariance (bitwise).
+Mutation tests at the end plant plausible mistakes in the oracle and check
+that at least one pin catches each.
+"""
+
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle.verify_oracle as vo
+from speculative_decoding_tree_verify_amd import inputs as gen
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "worked_tree_example.json")
+
+
+def _bf16(x):
+    return gen.f32_to_bf16_bits(np.asarray(x, dtype=np.float32))
+
+
+def _small_case(parent, L, H, dqk, dv, seed, pool_extra=5):
+    """Small random case with arbitrary dims; returns oracle-ready arrays."""
+    rng = np.random.default_rng(seed)
+    N = len(parent)
+    P = L + N + pool_extra + 1
+    slots = rng.permutation(np.arange(1, P))[: L + N]
+    pool = np.full((P, dqk), 0x7FC0, dtype=np.uint16)          # NaN poison in unused slots
+    pool[slots] = _bf16(rng.standard_normal((L + N, dqk)) * 0.7)
+    q = _bf16(rng.standard_normal((N, H, dqk)) * 0.7)
+    return dict(q_bits=q, pool_bits=pool, prefix_slot_idx=slots[:L].astype(np.int32),
+                tree_slot_idx=slots[L:].astype(np.int32), parent=np.asarray(parent, np.int32),
+                cu_prefix=np.array([0, L], np.int32), cu_tree=np.array([0, N], np.int32))
+
+
+def _brute(case, scale, dv):
+    """Explicit per-node key lists + pure-Python fsum arithmetic."""
+    q = vo.bf16_bits_to_f64(case["q_bits"])
+    pool = vo.bf16_bits_to_f64(case["pool_bits"])
+    parent = [int(x) for x in case["parent"]]
+    N, H, _ = q.shape
+    out = np.zeros((N, H, dv))
+    lse = np.zeros((N, H))
+    for t in range(N):
+        path = []
+        j = t
+        while j != -1:               # walk to the root
+            path.append(j)
+            j = parent[j]
+        slots = [int(s) for s in case["prefix_slot_idx"]] + [int(case["tree_slot_idx"][j]) for j in reversed(path)]
+        for h in range(H):
+            qv = [float(x) for x in q[t, h]]
+            scores = [scale * math.fsum(a * b for a, b in zip(qv, pool[s])) for s in slots]
+            m = max(scores)
+            l = m + math.log(math.fsum(math.exp(s - m) for s in scores))
+            lse[t, h] = l
+            w = [math.exp(s - l) for s in scores]
+            for d in range(dv):
+                out[t, h, d] = math.fsum(wi * pool[s][d] for wi, s in zip(w, slots))
+    return out, lse
+
+
+def _run(case, scale, dv):
+    return vo.verify(case["q_bits"], case["pool_bits"], case["prefix_slot_idx"], case["tree_slot_idx"],
+                     case["parent"], case["cu_prefix"], case["cu_tree"], scale, dv)
+
+
+# --------------------------------------------------------------------------
+
+def test_golden_worked_example():
+    fx = json.load(open(GOLDEN))
+    P, dqk = fx["pool_slots"], fx["d_qk"]
+    pool = np.full((P, dqk), 0x7FC0, dtype=np.uint16)
+    names = ["p0", "p1", "n0", "n1", "n2"]
+    slots = fx["prefix_slot_idx"] + fx["tree_slot_idx"]
+    for nm, s in zip(names, slots):
+        pool[s] = _bf16(fx["keys_logical"][nm])
+    q = _bf16(fx["q"])
+    out, lse = vo.verify(q, pool, np.array(fx["prefix_slot_idx"], np.int32), np.array(fx["tree_slot_idx"], np.int32),
+                         np.array(fx["parent"], np.int32), np.array([0, fx["prefix_len"]], np.int32),
+                         np.array([0, len(fx["parent"])], np.int32), fx["scale"], fx["d_v"])
+    env = {"e": math.e, "log": math.log, "__builtins__": {}}
+    exp_lse = np.array([[eval(s, env) for s in row] for row in fx["expected_lse"]])
+    exp_out = np.array([[[eval(s, env) for s in hv] for hv in row] for row in fx["expected_out"]])
+    np.testing.assert_allclose(lse, exp_lse, rtol=0, atol=1e-14)
+    np.testing.assert_allclose(out, exp_out, rtol=0, atol=1e-14)
+
+
+@pytest.mark.parametrize("N", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("L", [0, 1, 3])
+def test_bruteforce_every_small_tree(N, L):
+    scale = 0.37
+    for k, parent in enumerate(gen.all_parent_arrays(N)):
+        case = _small_case(parent, L, H=2, dqk=12, dv=8, seed=100 * N + 10 * L + k)
+        out, lse = _run(case, scale, 8)
+        bo, bl = _brute(case, scale, 8)
+        np.testing.assert_allclose(lse, bl, rtol=0, atol=1e-12)
+        np.testing.assert_allclose(out, bo, rtol=0, atol=1e-12)
+
+
+def test_tree_count_is_factorial():
+    # parent[i] ranges over i choices -> (N-1)! trees
+    assert sum(1 for _ in gen.all_parent_arrays(5)) == 24
+
+
+@pytest.mark.parametrize("seed", [1, 2, 3])
+def test_bruteforce_full_dims_random_trees(seed):
+    rng = np.random.default_rng(seed)
+    N = int(rng.integers(2, 13))
+    parent = gen.random_tree(N, rng)
+    case = _small_case(parent, L=int(rng.integers(0, 6)), H=2, dqk=576, dv=512, seed=seed)
+    scale = gen.SOFTMAX_SCALE
+    out, lse = _run(case, scale, 512)
+    bo, bl = _brute(case, scale, 512)
+    np.testing.assert_allclose(lse, bl, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(out, bo, rtol=0, atol=1e-12)
+
+
+def test_chain_equals_causal_sdpa():
+    torch = pytest.importorskip("torch")
+    L, N, H = 37, 9, 3
+    parent = np.arange(-1, N - 1, dtype=np.int32)
+    case = _small_case(parent, L, H, 576, 512, seed=11)
+    scale = gen.SOFTMAX_SCALE
+    out, _ = _run(case, scale, 512)
+    q = torch.from_numpy(vo.bf16_bits_to_f64(case["q_bits"])).permute(1, 0, 2)            # [H, N, d]
+    slots = np.concatenate([case["prefix_slot_idx"], case["tree_slot_idx"]]).astype(np.int64)
+    k = torch.from_numpy(vo.bf16_bits_to_f64(case["pool_bits"][slots]))                   # [L+N, d]
+    kk = k.unsqueeze(0).expand(H, -1, -1)
+    vv = k[:, :512].unsqueeze(0).expand(H, -1, -1)
+    # bottom-right aligned causal mask: query t sits at position L + t
+    allowed = torch.arange(L + N)[None, :] <= (L + torch.arange(N))[:, None]
+    ref = torch.nn.functional.scaled_dot_product_attention(q, kk, vv, attn_mask=allowed, scale=scale)
+    np.testing.assert_allclose(out, ref.permute(1, 0, 2).numpy(), rtol=0, atol=1e-12)
+
+
+def test_q_zero_closed_form():
+    rng = np.random.default_rng(5)
+    parent = gen.bounded_tree(20, rng, max_depth=5, max_children=3)
+    L = 7
+    case = _small_case(parent, L, H=2, dqk=576, dv=512, seed=5)
+    case["q_bits"][:] = 0
+    out, lse = _run(case, gen.SOFTMAX_SCALE, 512)
+    depth = gen.tree_depths(parent)
+    pool = vo.bf16_bits_to_f64(case["pool_bits"])
+    for t in range(len(parent)):
+        np.testing.assert_allclose(lse[t], math.log(L + depth[t] + 1), rtol=0, atol=1e-14)
+        rows = list(case["prefix_slot_idx"])
+        j = t
+        while j != -1:
+            rows.append(case["tree_slot_idx"][j])
+            j = parent[j]
+        mean = np.array([math.fsum(pool[s][d] for s in rows) / len(rows) for d in range(512)])
+        for h in range(2):
+            np.testing.assert_allclose(out[t, h], mean, rtol=0, atol=1e-14)
+
+
+def test_root_only_no_prefix():
+    case = _small_case(np.array([-1], np.int32), 0, H=4, dqk=576, dv=512, seed=9)
+    out, lse = _run(case, gen.SOFTMAX_SCALE, 512)
+    k = vo.bf16_bits_to_f64(case["pool_bits"][case["tree_slot_idx"][0]])
+    q = vo.bf16_bits_to_f64(case["q_bits"][0])
+    for h in range(4):
+        assert np.array_equal(out[0, h], k[:512])
+        assert abs(lse[0, h] - gen.SOFTMAX_SCALE * math.fsum(q[h] * k)) < 1e-14
+
+
+def test_planted_visible_and_hidden_keys():
+    parent = gen.chain_plus_branch(chain=5, branch_parent=1)   # node 5 is a sibling of node 2
+    L = 16
+    case = _small_case(parent, L, H=1, dqk=576, dv=512, seed=21)
+    pool = case["pool_bits"]
+    keyf = lambda j: vo.bf16_bits_to_f64(pool[case["tree_slot_idx"][j]])
+    alpha = 60.0
+    # node 4 (chain 0-1-2-3-4): plant its ancestor 2 -> out ~ V[2]
+    case["q_bits"][4, 0] = _bf16(alpha * keyf(2))
+    # node 3: plant hidden sibling-branch node 5 -> out must stay far from V[5]
+    case["q_bits"][3, 0] = _bf16(alpha * keyf(5))
+    out, _ = _run(case, gen.SOFTMAX_SCALE, 512)
+    np.testing.assert_allclose(out[4, 0], keyf(2)[:512], rtol=0, atol=1e-9)
+    assert np.abs(out[3, 0] - keyf(5)[:512]).max() > 0.1
+
+
+def test_split_merge_equals_unsplit():
+    rng = np.random.default_rng(3)
+    R, n, d = 6, 40, 24
+    qr = rng.standard_normal((R, d))
+    keys = rng.standard_normal((n, d))
+    full_o, full_l = vo.attend(qr, keys, 0.8, 10)
+    cuts = [0, 0, 1, 1, 7, 19, 20, 33, 40, 40]      # includes empty and 1-key parts
+    parts = [vo.attend(qr, keys[a:b], 0.8, 10) for a, b in zip(cuts[:-1], cuts[1:])]
+    mo, ml = vo.merge_partials(parts)
+    np.testing.assert_allclose(ml, full_l, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(mo, full_o, rtol=0, atol=1e-12)
+
+
+def test_prefix_and_tree_partials_merge_to_verify():
+    rng = np.random.default_rng(4)
+    parent = gen.random_tree(7, rng)
+    case = _small_case(parent, 50, H=3, dqk=576, dv=512, seed=4)
+    s = gen.SOFTMAX_SCALE
+    out, lse = _run(case, s, 512)
+    args = (case["q_bits"], case["pool_bits"], case["prefix_slot_idx"], case["cu_prefix"], case["cu_tree"], 0)
+    parts = [vo.prefix_partial(*args, a, b, s) for a, b in [(0, 20), (20, 21), (21, 50), (50, 50)]]
+    parts.append(vo.tree_partial(case["q_bits"], case["pool_bits"], case["tree_slot_idx"], case["parent"],
+                                 case["cu_tree"], 0, s))
+    mo, ml = vo.merge_partials([(o.reshape(-1, 512), l.reshape(-1)) for o, l in parts])
+    np.testing.assert_allclose(ml.reshape(lse.shape), lse, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(mo.reshape(out.shape), out, rtol=0, atol=1e-12)
+
+
+def test_slot_permutation_invariance():
+    rng = np.random.default_rng(8)
+    parent = gen.random_tree(6, rng)
+    case = _small_case(parent, 30, H=2, dqk=576, dv=512, seed=8)
+    out, lse = _run(case, gen.SOFTMAX_SCALE, 512)
+    P = case["pool_bits"].shape[0]
+    perm = rng.permutation(P)                         # new slot of old slot s is perm[s]
+    pool2 = np.empty_like(case["pool_bits"])
+    pool2[perm] = case["pool_bits"]
+    case2 = dict(case, pool_bits=pool2, prefix_slot_idx=perm[case["prefix_slot_idx"]].astype(np.int32),
+                 tree_slot_idx=perm[case["tree_slot_idx"]].astype(np.int32))
+    out2, lse2 = _run(case2, gen.SOFTMAX_SCALE, 512)
+    assert np.array_equal(out, out2) and np.array_equal(lse, lse2)
+
+
+def test_batch_requests_are_independent():
+    rng = np.random.default_rng(12)
+    pa, pb = gen.random_tree(4, rng), gen.random_tree(3, rng)
+    ca = _small_case(pa, 9, 2, 576, 512, seed=1)
+    cb = _small_case(pb, 5, 2, 576, 512, seed=2)
+    # stack the two requests into one pool
+    Pa = ca["pool_bits"].shape[0]
+    pool = np.concatenate([ca["pool_bits"], cb["pool_bits"]])
+    q = np.concatenate([ca["q_bits"], cb["q_bits"]])
+    pre = np.concatenate([ca["prefix_slot_idx"], cb["prefix_slot_idx"] + Pa]).astype(np.int32)
+    tre = np.concatenate([ca["tree_slot_idx"], cb["tree_slot_idx"] + Pa]).astype(np.int32)
+    par = np.concatenate([pa, pb]).astype(np.int32)
+    out, lse = vo.verify(q, pool, pre, tre, par, np.array([0, 9, 14], np.int32), np.array([0, 4, 7], np.int32),
+                         gen.SOFTMAX_SCALE)
+    oa, la = _run(ca, gen.SOFTMAX_SCALE, 512)
+    ob, lb = _run(cb, gen.SOFTMAX_SCALE, 512)
+    assert np.array_equal(out[:4], oa) and np.array_equal(out[4:], ob)
+    assert np.array_equal(lse[:4], la) and np.array_equal(lse[4:], lb)
+
+
+def test_gather_rows_matches_take():
+    rng = np.random.default_rng(0)
+    pool = rng.integers(0, 65536, size=(100, 576), dtype=np.uint16)
+    idx = rng.integers(0, 100, size=57)
+    assert np.array_equal(vo.gather_rows(pool, idx), np.take(pool, idx, axis=0))
+
+
+# --------------------------------------------------------------------------
+# mutation tests: plausible mistakes planted in the oracle must be caught
+# --------------------------------------------------------------------------
+
+def _pins_pass():
+    """Run the cheap pins; return False as soon as one fails."""
+    checks = [test_golden_worked_example, test_chain_equals_causal_sdpa, test_q_zero_closed_form,
+              test_root_only_no_prefix, test_planted_visible_and_hidden_keys,
+              lambda: test_bruteforce_every_small_tree(4, 1)]
+    for c in checks:
+        try:
+            c()
+        except AssertionError:
+            return False
+    return True
+
+
+def test_pins_pass_unmutated():
+    assert _pins_pass()
+
+
+def test_mutation_self_excluded(monkeypatch):
+    orig = vo.ancestors_or_self
+    monkeypatch.setattr(vo, "ancestors_or_self", lambda p, t: orig(p, t)[1:] or [t])
+    assert not _pins_pass()
+
+
+def test_mutation_siblings_visible(monkeypatch):
+    def vis(parent, L):
+        n = len(parent)
+        v = np.zeros((n, L + n), bool)
+        v[:, :L] = True
+        for t in range(n):
+            for j in range(t + 1):           # everything up to t: causal over the flattened tree
+                v[t, L + j] = True
+        return v
+    monkeypatch.setattr(vo, "visibility", vis)
+    assert not _pins_pass()
+
+
+def test_mutation_v_from_last_columns(monkeypatch):
+    orig = vo.attend
+    def attend(qrows, keys, scale, d_v=512, vis=None):
+        o, l = orig(qrows, keys[:, ::-1].copy(), scale, d_v, vis)   # wrong V columns (and key order)
+        return o, l
+    monkeypatch.setattr(vo, "attend", attend)
+    assert not _pins_pass()
+
+
+def test_mutation_scale_dropped(monkeypatch):
+    orig = vo.attend
+    monkeypatch.setattr(vo, "attend", lambda q, k, s, d_v=512, vis=None: orig(q, k, 1.0, d_v, vis))
+    assert not _pins_pass()
+
+
+def test_mutation_lse_base2(monkeypatch):
+    orig = vo.attend
+    def attend(q, k, s, d_v=512, vis=None):
+        o, l = orig(q, k, s, d_v, vis)
+        return o, l / math.log(2)
+    monkeypatch.setattr(vo, "attend", attend)
+    assert not _pins_pass()
+
+
+def test_mutation_prefix_masked_causally(monkeypatch):
+    orig = vo.visibility
+    def vis(parent, L):
+        v = orig(parent, L)
+        n = len(parent)
+        for t in range(n):
+            v[t, max(0, L - n + t + 1):L] = False     # drops the last prefix keys for early nodes
+        return v
+    monkeypatch.setattr(vo, "visibility", vis)
+    assert not _pins_pass()
