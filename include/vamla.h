@@ -1,0 +1,205 @@
+/*
+ * vamla.h - C ABI of libvamla: DDTree verify attention for MLA on MI355X (gfx950).
+ *
+ * What the library computes.  A batch of B requests; request b has a prefix of
+ * L_b tokens and a drafted tree of N_b nodes (N_b <= 65).  Every token's latent
+ * KV is one 576-wide bf16 row (512 latent + 64 rope) in a page_size=1 slot pool;
+ * V is the first 512 columns of the same row (one latent KV head, head_dim 576).
+ * For node t of request b and head h:
+ *
+ *   visible keys  = all L_b prefix rows  +  tree rows of t and of every ancestor of t
+ *   s_l  = softmax_scale * <q[t,h,:], K_l>
+ *   lse  = ln sum_l exp(s_l)              (natural log of the scaled scores)
+ *   out  = sum_l exp(s_l - lse) * V_l     (rounded to bf16, nearest-even)
+ *
+ * Sources (web pages on DDTree verify attention):
+ *   - "Mapping the Optimization Landscape for DDTree Verify Attention",
+ *     "Input Knowledge Required to Understand This Message", item 1: each draft
+ *     token attends only to its ancestors (read here as ancestors-or-self).
+ *   - "The Architecture Detective: Uncovering FlashMLA's Potential for Blackwell
+ *     DDTree Verification", "The Message in Full": the prefix is attended densely
+ *     by every node with no causal constraint (causal=False, cache_seqlens=L);
+ *     RoPE is applied upstream; num_heads_k=1, head_dim=576; the work splits into
+ *     a dense prefix pass, a small masked tree-tail pass and a merge of the two.
+ *   - "The Anatomy of a Kernel Investigation", "The Reasoning Process: A Deep
+ *     Dive", Phase 2: the split-KV design merged through the log-sum-exp of
+ *     partial attention states.
+ *   - same page, "The Bash Command": page_size=1 pool with slot 0 as padding.
+ *
+ * Conventions for every entry point:
+ *   - All tensors are row-major and densely packed.  bf16 values are passed as
+ *     their 16-bit patterns (uint16_t).
+ *   - Pointers marked "device" must be HIP device (or managed) memory readable
+ *     by the GPU that is current when the call is made.  "host" pointers are
+ *     read during the call only.
+ *   - The caller owns every buffer, including the workspace.  The library never
+ *     allocates or frees memory, never synchronises the stream, and keeps no
+ *     pointer after returning.  All GPU work is enqueued on `stream` (a
+ *     hipStream_t passed as void*; NULL = the default stream).
+ *   - Return value: VAMLA_OK (0) or a negative vamla_status.  Nothing throws or
+ *     aborts across the ABI.  On an error return nothing has been enqueued,
+ *     except VAMLA_ERR_LAUNCH, which reports a failed kernel launch.
+ *   - Contents of index arrays (slot indices in [0, pool_slots), parent arrays,
+ *     cumulative lengths) are the caller's contract: the GPU path does not check
+ *     them.  vamla_validate checks them on host copies.
+ *   - Entry points are reentrant; concurrent calls must use distinct workspaces.
+ */
+#ifndef VAMLA_H
+#define VAMLA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define VAMLA_D_QK 576          /* latent (512) + rope (64) */
+#define VAMLA_D_V 512           /* V = columns [0, 512) of the same row */
+#define VAMLA_MAX_TREE 65       /* root + up to 64 drafted nodes */
+#define VAMLA_MAX_HEADS 128
+#define VAMLA_KEY_TILE 64       /* chunk sizes are multiples of this */
+#define VAMLA_ROW_TILE 128      /* query rows per prefix work item */
+
+typedef enum vamla_status {
+  VAMLA_OK = 0,
+  VAMLA_ERR_INVALID_ARG = -1,    /* null pointer, negative size, bad flag */
+  VAMLA_ERR_UNSUPPORTED = -2,    /* shape outside what the kernels handle (d_qk, d_v, H, N) */
+  VAMLA_ERR_WORKSPACE = -3,      /* workspace missing or smaller than vamla_workspace_size */
+  VAMLA_ERR_ARCH = -4,           /* current device is not gfx950 */
+  VAMLA_ERR_LAUNCH = -5,         /* a kernel launch failed */
+  VAMLA_ERR_INVALID_TREE = -6,   /* vamla_validate: parent array not topological, or not one root */
+  VAMLA_ERR_INVALID_SLOT = -7,   /* vamla_validate: slot index outside [0, pool_slots) */
+  VAMLA_ERR_INVALID_LENGTHS = -8 /* vamla_validate: cumulative lengths inconsistent with params */
+} vamla_status;
+
+/*
+ * Problem description shared by all verify entry points.
+ *
+ * Query row order: global row g = t * num_heads + h for tree node t (global
+ * node index over the batch, t in [0, total_tree)) and head h.  Request b owns
+ * nodes [cu_tree[b], cu_tree[b+1]) and prefix tokens [cu_prefix[b], cu_prefix[b+1])
+ * of prefix_slot_idx.
+ */
+typedef struct vamla_params {
+  int32_t batch;            /* B >= 1 */
+  int32_t num_heads;        /* H in [1, 128] */
+  int32_t d_qk;             /* must be 576 */
+  int32_t d_v;              /* must be 512 */
+  int64_t pool_slots;       /* P >= 1: rows in kv_pool */
+  float softmax_scale;      /* sigma, applied to q.k before the exponential */
+  int32_t max_tree;         /* >= every N_b, in [1, 65] (planning bound) */
+  int32_t total_tree;       /* T = cu_tree[B] >= 1 */
+  int64_t max_prefix;       /* >= every L_b (planning bound), >= 0 */
+  int64_t total_prefix;     /* cu_prefix[B]; used to choose the chunk size */
+  int32_t chunk;            /* prefix keys per split; multiple of 64, or 0 = choose automatically */
+  uint32_t flags;           /* reserved, must be 0 */
+  const int32_t* cu_prefix; /* device [B+1], cu_prefix[0] = 0, non-decreasing */
+  const int32_t* cu_tree;   /* device [B+1], cu_tree[0] = 0, increasing (N_b >= 1) */
+  void* workspace;          /* device, 256-byte aligned, >= vamla_workspace_size bytes */
+  size_t workspace_bytes;
+} vamla_params;
+
+/* Work decomposition the library derives from vamla_params (host only). */
+typedef struct vamla_plan_info {
+  int32_t chunk;            /* prefix keys per split (multiple of 64) */
+  int32_t row_tiles;        /* ceil(max_tree * H / 128): row tiles per request */
+  int32_t max_chunks;       /* ceil(max_prefix / chunk), >= 1 */
+  int32_t grid_items;       /* prefix kernel grid (B * row_tiles * max_chunks, padded to 8) */
+  /* workspace layout (byte offsets from vamla_params.workspace) */
+  size_t off_part_o;        /* float [B][row_tiles][max_chunks][128 d4][128 rows][4] */
+  size_t off_part_lse;      /* float [B][row_tiles][max_chunks][128 rows] */
+  size_t off_tail_o;        /* float [B][row_tiles][128 d4][128 rows][4] */
+  size_t off_tail_lse;      /* float [B][row_tiles][128 rows] */
+  size_t workspace_bytes;   /* total */
+} vamla_plan_info;
+
+/* Human-readable name of a status code (static string). */
+const char* vamla_status_string(int status);
+
+/*
+ * Derives the work decomposition and workspace layout.  Host only; makes no
+ * HIP call, so it works without a GPU.  Returns VAMLA_ERR_INVALID_ARG or
+ * VAMLA_ERR_UNSUPPORTED for parameters the kernels cannot take.  Pointer fields
+ * of *p are not read.
+ */
+int vamla_plan(const vamla_params* p, vamla_plan_info* out);
+
+/* Workspace bytes verify_attn_mla needs for *p (host only, like vamla_plan). */
+int vamla_workspace_size(const vamla_params* p, size_t* bytes);
+
+/*
+ * Host-side check of the index data a caller is about to pass (host copies):
+ *   h_cu_prefix[B+1], h_cu_tree[B+1]: start at 0, prefix non-decreasing, tree
+ *     increasing; totals match total_prefix / total_tree; every N_b <= max_tree,
+ *     every L_b <= max_prefix;
+ *   h_parent[T]: per request, parent[0] = -1 and 0 <= parent[i] < i;
+ *   h_prefix_slot_idx[total_prefix], h_tree_slot_idx[T] (either may be NULL to
+ *     skip): every slot in [0, pool_slots).
+ * Makes no HIP call.  Returns VAMLA_OK or the first violation's code.
+ */
+int vamla_validate(const vamla_params* p, const int32_t* h_parent, const int32_t* h_cu_tree,
+                   const int32_t* h_cu_prefix, const int32_t* h_prefix_slot_idx,
+                   const int32_t* h_tree_slot_idx);
+
+/*
+ * The verify step: prefix split-KV pass, masked tree-tail pass and LSE merge,
+ * three kernels enqueued on `stream`.
+ *   q               device bf16 [T, H, 576]: queries of every node (RoPE applied)
+ *   kv_pool         device bf16 [P, 576]: latent rows; V = first 512 columns
+ *   prefix_slot_idx device int32 [total_prefix]: pool slot of each prefix token
+ *                   (may be NULL when total_prefix == 0)
+ *   tree_slot_idx   device int32 [T]: pool slot of each tree node's own KV row
+ *   parent          device int32 [T]: request-local parent, root = -1
+ *   out             device bf16 [T, H, 512] (fully overwritten)
+ *   lse             device float [T, H] (fully overwritten)
+ * out and lse must not alias any input or the workspace.  Chunk boundaries are
+ * fixed by logical token position, so the result does not depend on where the
+ * rows sit in the pool (scrambled and contiguous pools give identical bits).
+ */
+int verify_attn_mla(const vamla_params* p, const uint16_t* q, const uint16_t* kv_pool,
+                    const int32_t* prefix_slot_idx, const int32_t* tree_slot_idx,
+                    const int32_t* parent, uint16_t* out, float* lse, void* stream);
+
+/*
+ * Stage 1 alone: split-KV attention of every row over each prefix chunk,
+ * written to the workspace (part_o normalised by its own softmax sum, part_lse
+ * natural log; layout in vamla_plan_info).  Chunk s of request b covers prefix
+ * tokens [s*chunk, min((s+1)*chunk, L_b)); chunks at or past L_b are not written.
+ * Split-KV design: "The Anatomy of a Kernel Investigation", Phase 2.
+ */
+int vamla_prefix_partials(const vamla_params* p, const uint16_t* q, const uint16_t* kv_pool,
+                          const int32_t* prefix_slot_idx, void* stream);
+
+/*
+ * Stage 2 alone: attention of every row over its own tree keys under the
+ * ancestor-or-self mask, written to the workspace tail slots.  "The Architecture
+ * Detective ...", "The Message in Full": the small masked tree-tail pass.
+ */
+int vamla_tree_tail(const vamla_params* p, const uint16_t* q, const uint16_t* kv_pool,
+                    const int32_t* tree_slot_idx, const int32_t* parent, void* stream);
+
+/*
+ * Stage 3 alone: merges the prefix chunk partials and the tail partial in the
+ * workspace into out (bf16) and lse (float): lse = ln sum_s exp(lse_s),
+ * out = sum_s exp(lse_s - lse) * o_s.  Same pages: merging partial attention
+ * states by their log-sum-exp.
+ */
+int vamla_lse_merge(const vamla_params* p, uint16_t* out, float* lse, void* stream);
+
+/*
+ * Slot compaction (defragmentation) gather: dst[l, :] = kv_pool[idx[l], :] for
+ * l in [0, n), bit-exact 1152-byte rows, 64-bit addressing.
+ *   kv_pool device bf16 [*, 576]; idx device int32 [n] (slots must be valid);
+ *   dst device bf16 [n, 576], must not overlap kv_pool rows named in idx.
+ * "The Architecture Detective ...", "Defragmentation: Separating Signal from
+ * Noise": compaction of scattered KV slots, secondary to the kernel itself.
+ */
+int vamla_slot_gather(const uint16_t* kv_pool, const int32_t* idx, int64_t n, uint16_t* dst,
+                      void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VAMLA_H */

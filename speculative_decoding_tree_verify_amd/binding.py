@@ -1,0 +1,308 @@
+"""ctypes binding of libvamla.so (C ABI in include/vamla.h).
+
+Argument marshalling only: tensors are passed as device pointers together with
+the current HIP stream of torch; every step of the verify path runs in the HIP
+kernels behind the ABI.  Importing this module does not load the library; the
+first call does, and raises if libvamla.so has not been built.  There is no
+CPU fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional, Tuple
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG_DIR, "libvamla.so")
+
+D_QK = 576
+D_V = 512
+MAX_TREE = 65
+MAX_HEADS = 128
+KEY_TILE = 64
+ROW_TILE = 64
+
+STATUS = {
+    0: "VAMLA_OK", -1: "VAMLA_ERR_INVALID_ARG", -2: "VAMLA_ERR_UNSUPPORTED", -3: "VAMLA_ERR_WORKSPACE",
+    -4: "VAMLA_ERR_ARCH", -5: "VAMLA_ERR_LAUNCH", -6: "VAMLA_ERR_INVALID_TREE", -7: "VAMLA_ERR_INVALID_SLOT",
+    -8: "VAMLA_ERR_INVALID_LENGTHS",
+}
+
+EXPORTS = ("vamla_status_string", "vamla_plan", "vamla_workspace_size", "vamla_validate", "verify_attn_mla",
+           "vamla_prefix_partials", "vamla_tree_tail", "vamla_lse_merge", "vamla_slot_gather")
+
+
+class VamlaParams(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("num_heads", ctypes.c_int32),
+        ("d_qk", ctypes.c_int32),
+        ("d_v", ctypes.c_int32),
+        ("pool_slots", ctypes.c_int64),
+        ("softmax_scale", ctypes.c_float),
+        ("max_tree", ctypes.c_int32),
+        ("total_tree", ctypes.c_int32),
+        ("max_prefix", ctypes.c_int64),
+        ("total_prefix", ctypes.c_int64),
+        ("chunk", ctypes.c_int32),
+        ("flags", ctypes.c_uint32),
+        ("cu_prefix", ctypes.c_void_p),
+        ("cu_tree", ctypes.c_void_p),
+        ("workspace", ctypes.c_void_p),
+        ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+
+class VamlaPlanInfo(ctypes.Structure):
+    _fields_ = [
+        ("chunk", ctypes.c_int32),
+        ("row_tiles", ctypes.c_int32),
+        ("max_chunks", ctypes.c_int32),
+        ("grid_items", ctypes.c_int32),
+        ("off_part_o", ctypes.c_size_t),
+        ("off_part_lse", ctypes.c_size_t),
+        ("off_tail_o", ctypes.c_size_t),
+        ("off_tail_lse", ctypes.c_size_t),
+        ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+
+class VamlaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {STATUS.get(status, status)} ({_msg(status)})")
+
+
+_LIB: Optional[ctypes.CDLL] = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libvamla.so once; raise if it is missing (no fallback path)."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m speculative_decoding_tree_verify_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64, P = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.POINTER
+    L.vamla_status_string.restype = ctypes.c_char_p
+    L.vamla_status_string.argtypes = [ctypes.c_int]
+    L.vamla_plan.argtypes = [P(VamlaParams), P(VamlaPlanInfo)]
+    L.vamla_workspace_size.argtypes = [P(VamlaParams), P(ctypes.c_size_t)]
+    L.vamla_validate.argtypes = [P(VamlaParams), vp, vp, vp, vp, vp]
+    L.verify_attn_mla.argtypes = [P(VamlaParams), vp, vp, vp, vp, vp, vp, vp, vp]
+    L.vamla_prefix_partials.argtypes = [P(VamlaParams), vp, vp, vp, vp]
+    L.vamla_tree_tail.argtypes = [P(VamlaParams), vp, vp, vp, vp, vp]
+    L.vamla_lse_merge.argtypes = [P(VamlaParams), vp, vp, vp]
+    L.vamla_slot_gather.argtypes = [vp, vp, i64, vp, vp]
+    for name in EXPORTS:
+        if name != "vamla_status_string":
+            getattr(L, name).restype = ctypes.c_int
+    _LIB = L
+    return L
+
+
+def _msg(status: int) -> str:
+    try:
+        return lib().vamla_status_string(status).decode()
+    except Exception:  # library not loadable: plain code only
+        return str(status)
+
+
+def _check(status: int, where: str) -> None:
+    if status != 0:
+        raise VamlaError(status, where)
+
+
+# --------------------------------------------------------------------------
+# parameters
+# --------------------------------------------------------------------------
+
+@dataclass
+class Problem:
+    """Host-known scalars of one verify call (no device reads needed)."""
+    batch: int
+    num_heads: int
+    pool_slots: int
+    softmax_scale: float
+    max_tree: int
+    total_tree: int
+    max_prefix: int
+    total_prefix: int
+    chunk: int = 0
+
+    def params(self, cu_prefix_ptr: int = 0, cu_tree_ptr: int = 0, workspace_ptr: int = 0,
+               workspace_bytes: int = 0) -> VamlaParams:
+        return VamlaParams(self.batch, self.num_heads, D_QK, D_V, self.pool_slots, self.softmax_scale,
+                           self.max_tree, self.total_tree, self.max_prefix, self.total_prefix, self.chunk, 0,
+                           cu_prefix_ptr, cu_tree_ptr, workspace_ptr, workspace_bytes)
+
+    @staticmethod
+    def from_host(cu_prefix, cu_tree, num_heads: int, pool_slots: int, softmax_scale: float,
+                  chunk: int = 0) -> "Problem":
+        """Derive the scalars from host copies of the cumulative length arrays."""
+        cp = [int(x) for x in cu_prefix]
+        ct = [int(x) for x in cu_tree]
+        B = len(cp) - 1
+        return Problem(batch=B, num_heads=num_heads, pool_slots=pool_slots, softmax_scale=float(softmax_scale),
+                       max_tree=max(ct[b + 1] - ct[b] for b in range(B)), total_tree=ct[-1],
+                       max_prefix=max(cp[b + 1] - cp[b] for b in range(B)), total_prefix=cp[-1], chunk=chunk)
+
+
+def plan(prob: Problem) -> VamlaPlanInfo:
+    info = VamlaPlanInfo()
+    p = prob.params()
+    _check(lib().vamla_plan(ctypes.byref(p), ctypes.byref(info)), "vamla_plan")
+    return info
+
+
+def workspace_size(prob: Problem) -> int:
+    n = ctypes.c_size_t(0)
+    p = prob.params()
+    _check(lib().vamla_workspace_size(ctypes.byref(p), ctypes.byref(n)), "vamla_workspace_size")
+    return int(n.value)
+
+
+def validate(prob: Problem, parent, cu_tree, cu_prefix, prefix_slot_idx=None, tree_slot_idx=None) -> int:
+    """Host-side validation of index arrays (numpy int32, contiguous).  Returns the status."""
+    import numpy as np
+
+    def ptr(a):
+        if a is None:
+            return None
+        a = np.ascontiguousarray(a, dtype=np.int32)
+        keep.append(a)
+        return a.ctypes.data
+    keep = []
+    p = prob.params()
+    return int(lib().vamla_validate(ctypes.byref(p), ptr(parent), ptr(cu_tree), ptr(cu_prefix),
+                                    ptr(prefix_slot_idx), ptr(tree_slot_idx)))
+
+
+# --------------------------------------------------------------------------
+# device calls (torch tensors on the current HIP device)
+# --------------------------------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t) -> int:
+    if t is None:
+        return 0
+    if not t.is_cuda:
+        raise ValueError("tensor must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream=None) -> int:
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _bits(t, what: str):
+    """bf16 tensors are passed as their 16-bit patterns."""
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return t
+    if t.dtype in (torch.int16, torch.uint16):
+        return t
+    raise TypeError(f"{what} must be bfloat16 (or its 16-bit pattern), got {t.dtype}")
+
+
+class Workspace:
+    """Caller-owned scratch sized by vamla_workspace_size (allocated by torch)."""
+
+    def __init__(self, prob: Problem, device=None):
+        torch = _torch()
+        self.nbytes = workspace_size(prob)
+        # 256-byte alignment: torch's caching allocator returns 512-byte aligned blocks
+        self.buf = torch.empty(max(self.nbytes, 256), dtype=torch.uint8, device=device or "cuda")
+        assert self.buf.data_ptr() % 256 == 0
+
+    @property
+    def ptr(self) -> int:
+        return self.buf.data_ptr()
+
+
+def _params(prob: Problem, cu_prefix, cu_tree, ws: Workspace) -> VamlaParams:
+    torch = _torch()
+    for t, nm in ((cu_prefix, "cu_prefix"), (cu_tree, "cu_tree")):
+        if t.dtype != torch.int32:
+            raise TypeError(f"{nm} must be int32")
+    return prob.params(_ptr(cu_prefix), _ptr(cu_tree), ws.ptr, ws.nbytes)
+
+
+def verify_attn_mla(prob: Problem, q, kv_pool, prefix_slot_idx, tree_slot_idx, parent, cu_prefix, cu_tree,
+                    ws: Optional[Workspace] = None, out=None, lse=None, stream=None) -> Tuple[object, object]:
+    """out [T, H, 512] bf16, lse [T, H] fp32 for every tree node and head."""
+    torch = _torch()
+    ws = ws or Workspace(prob, q.device)
+    T, H = prob.total_tree, prob.num_heads
+    if out is None:
+        out = torch.empty((T, H, D_V), dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty((T, H), dtype=torch.float32, device=q.device)
+    p = _params(prob, cu_prefix, cu_tree, ws)
+    st = lib().verify_attn_mla(ctypes.byref(p), _ptr(_bits(q, "q")), _ptr(_bits(kv_pool, "kv_pool")),
+                               _ptr(prefix_slot_idx) if prob.total_prefix else None, _ptr(tree_slot_idx),
+                               _ptr(parent), _ptr(out), _ptr(lse), _stream(stream))
+    _check(st, "verify_attn_mla")
+    return out, lse
+
+
+def prefix_partials(prob: Problem, q, kv_pool, prefix_slot_idx, cu_prefix, cu_tree, ws: Workspace, stream=None):
+    p = _params(prob, cu_prefix, cu_tree, ws)
+    _check(lib().vamla_prefix_partials(ctypes.byref(p), _ptr(_bits(q, "q")), _ptr(_bits(kv_pool, "kv_pool")),
+                                       _ptr(prefix_slot_idx) if prob.total_prefix else None, _stream(stream)),
+           "vamla_prefix_partials")
+
+
+def tree_tail(prob: Problem, q, kv_pool, tree_slot_idx, parent, cu_prefix, cu_tree, ws: Workspace, stream=None):
+    p = _params(prob, cu_prefix, cu_tree, ws)
+    _check(lib().vamla_tree_tail(ctypes.byref(p), _ptr(_bits(q, "q")), _ptr(_bits(kv_pool, "kv_pool")),
+                                 _ptr(tree_slot_idx), _ptr(parent), _stream(stream)), "vamla_tree_tail")
+
+
+def lse_merge(prob: Problem, cu_prefix, cu_tree, ws: Workspace, out, lse, stream=None):
+    p = _params(prob, cu_prefix, cu_tree, ws)
+    _check(lib().vamla_lse_merge(ctypes.byref(p), _ptr(out), _ptr(lse), _stream(stream)), "vamla_lse_merge")
+
+
+def slot_gather(kv_pool, idx, dst=None, stream=None):
+    """dst[l] = kv_pool[idx[l]] (bit-exact)."""
+    torch = _torch()
+    n = idx.numel()
+    if dst is None:
+        dst = torch.empty((n, D_QK), dtype=kv_pool.dtype, device=kv_pool.device)
+    _check(lib().vamla_slot_gather(_ptr(_bits(kv_pool, "kv_pool")), _ptr(idx) if n else None, n,
+                                   _ptr(dst) if n else None, _stream(stream)), "vamla_slot_gather")
+    return dst
+
+
+def workspace_views(prob: Problem, ws: Workspace):
+    """Typed views of the workspace regions (for stage-level checks):
+    part_o [B, tiles, chunks, 128, 64, 4], part_lse [B, tiles, chunks, 64],
+    tail_o [B, tiles, 128, 64, 4], tail_lse [B, tiles, 64] (all float32)."""
+    torch = _torch()
+    info = plan(prob)
+    B, R, C = prob.batch, info.row_tiles, info.max_chunks
+    f = ws.buf.view(torch.float32) if ws.buf.numel() % 4 == 0 else ws.buf[: ws.buf.numel() // 4 * 4].view(torch.float32)
+
+    def region(off, shape):
+        n = 1
+        for s in shape:
+            n *= s
+        return f[off // 4: off // 4 + n].view(*shape)
+    return dict(plan=info,
+                part_o=region(info.off_part_o, (B, R, C, D_V // 4, ROW_TILE, 4)),
+                part_lse=region(info.off_part_lse, (B, R, C, ROW_TILE)),
+                tail_o=region(info.off_tail_o, (B, R, D_V // 4, ROW_TILE, 4)),
+                tail_lse=region(info.off_tail_lse, (B, R, ROW_TILE)))

@@ -1,0 +1,78 @@
+// Internal declarations shared by the HIP kernels and the host library.
+// Not part of the public ABI (include/vamla.h is).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace vamla {
+
+constexpr int kDqk = 576;                  // latent 512 + rope 64
+constexpr int kDv = 512;
+constexpr int kChunks16 = kDqk / 8;        // 72 sixteen-byte pieces per pool row
+constexpr int kKeyTile = 64;               // keys per LDS tile
+constexpr int kRowTile = 64;               // query rows per prefix work item (2 wave pairs x 32)
+constexpr int kD4 = kDv / 4;               // 128 float4 groups per output row
+constexpr int kTileBytes = kChunks16 * kKeyTile * 16;   // 73728 B of LDS per key tile
+constexpr int kMaxTree = 65;
+constexpr int kMaxHeads = 128;
+
+// Prefix split-KV pass.
+struct PrefixArgs {
+  const uint16_t* q;          // [T, H, 576] bf16
+  const uint16_t* pool;       // [P, 576] bf16
+  const int32_t* prefix_slot; // [total_prefix]
+  const int32_t* cu_prefix;   // [B+1]
+  const int32_t* cu_tree;     // [B+1]
+  float* part_o;              // [B][row_tiles][max_chunks][128 d4][64 rows][4]
+  float* part_lse;            // [B][row_tiles][max_chunks][64 rows]
+  int32_t num_heads;
+  int32_t chunk;
+  int32_t row_tiles;
+  int32_t max_chunks;
+  int32_t batch;
+  int32_t grid_items;         // multiple of 8
+  float scale_log2;           // softmax_scale * log2(e)
+};
+
+// Masked tree-tail pass.
+struct TailArgs {
+  const uint16_t* q;
+  const uint16_t* pool;
+  const int32_t* tree_slot;   // [T]
+  const int32_t* parent;      // [T], request-local
+  const int32_t* cu_tree;     // [B+1]
+  float* tail_o;              // [B][row_tiles][128 d4][64 rows][4]
+  float* tail_lse;            // [B][row_tiles][64 rows]
+  int32_t num_heads;
+  int32_t row_tiles;
+  int32_t batch;
+  int32_t total_tree;
+  float scale;
+};
+
+// LSE merge of prefix chunk partials and the tail partial.
+struct MergeArgs {
+  const float* part_o;
+  const float* part_lse;
+  const float* tail_o;
+  const float* tail_lse;
+  const int32_t* cu_prefix;
+  const int32_t* cu_tree;
+  uint16_t* out;              // [T, H, 512] bf16
+  float* lse;                 // [T, H]
+  int32_t num_heads;
+  int32_t chunk;
+  int32_t row_tiles;
+  int32_t max_chunks;
+  int32_t batch;
+};
+
+hipError_t launch_prefix_splitkv(const PrefixArgs& a, hipStream_t stream);
+hipError_t launch_tree_tail(const TailArgs& a, hipStream_t stream);
+hipError_t launch_lse_merge(const MergeArgs& a, hipStream_t stream);
+hipError_t launch_slot_gather(const uint16_t* pool, const int32_t* idx, int64_t n, uint16_t* dst,
+                              hipStream_t stream);
+
+}  // namespace vamla

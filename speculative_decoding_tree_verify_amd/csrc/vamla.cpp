@@ -1,0 +1,320 @@
+// Host side of libvamla: parameter checks, work planning, workspace layout and
+// kernel launches for DDTree verify attention (see include/vamla.h).
+//
+// Planning, workspace sizing and validation make no HIP call, so they run on a
+// host without a GPU.  The verify entry points enqueue kernels on the caller's
+// stream and never allocate, free or synchronise.
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <atomic>
+#include <cmath>
+#include <cstring>
+
+#include "kernels.h"
+#include "vamla.h"
+
+namespace {
+
+using namespace vamla;
+
+// Chunk choice assumes the full MI355X: 256 CUs, one prefix work item per CU
+// at a time (the item's key tiles fill the LDS).
+constexpr int64_t kCUs = 256;
+// Fixed cost of one prefix work item (loading its queries, writing its
+// partial), expressed in keys of streaming work.
+constexpr int64_t kItemOverheadKeys = 256;
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+int check_shape(const vamla_params* p) {
+  if (!p) return VAMLA_ERR_INVALID_ARG;
+  if (p->batch < 1 || p->pool_slots < 1 || p->max_prefix < 0 || p->total_prefix < 0 || p->total_tree < 1)
+    return VAMLA_ERR_INVALID_ARG;
+  if (p->flags != 0) return VAMLA_ERR_INVALID_ARG;
+  if (!(std::isfinite(p->softmax_scale))) return VAMLA_ERR_INVALID_ARG;
+  if (p->d_qk != VAMLA_D_QK || p->d_v != VAMLA_D_V) return VAMLA_ERR_UNSUPPORTED;
+  if (p->num_heads < 1 || p->num_heads > VAMLA_MAX_HEADS) return VAMLA_ERR_UNSUPPORTED;
+  if (p->max_tree < 1 || p->max_tree > VAMLA_MAX_TREE) return VAMLA_ERR_UNSUPPORTED;
+  if (p->chunk < 0 || p->chunk % VAMLA_KEY_TILE != 0) return VAMLA_ERR_INVALID_ARG;
+  // 32-bit index arithmetic inside the kernels
+  if (p->max_prefix > (int64_t)INT32_MAX - 2 * VAMLA_KEY_TILE || p->total_prefix > (int64_t)INT32_MAX)
+    return VAMLA_ERR_UNSUPPORTED;
+  if ((int64_t)p->total_tree * p->num_heads > (int64_t)INT32_MAX / VAMLA_D_V) return VAMLA_ERR_UNSUPPORTED;
+  if (p->pool_slots > (int64_t)UINT32_MAX) return VAMLA_ERR_UNSUPPORTED;
+  return VAMLA_OK;
+}
+
+int64_t choose_chunk(const vamla_params* p, int64_t row_tiles) {
+  if (p->chunk > 0) return p->chunk;
+  const int64_t maxL = p->max_prefix;
+  if (maxL <= VAMLA_KEY_TILE) return VAMLA_KEY_TILE;
+  const int64_t total = p->total_prefix > 0 ? p->total_prefix : maxL;
+  // Candidates: the longest prefix split into k chunks, k = 1, 2, ...; cost =
+  // rounds of work items over the CUs times the keys each item streams.
+  int64_t best_c = VAMLA_KEY_TILE, best_cost = INT64_MAX;
+  const int64_t kmax = std::min<int64_t>(ceil_div(maxL, VAMLA_KEY_TILE), 8192);
+  for (int64_t k = 1; k <= kmax; ++k) {
+    const int64_t c = ceil_div(ceil_div(maxL, k), VAMLA_KEY_TILE) * VAMLA_KEY_TILE;
+    // each request contributes its full chunks plus at most one partial one
+    const int64_t chunks =
+        std::min<int64_t>(ceil_div(total, c) + (p->batch - 1), (int64_t)p->batch * ceil_div(maxL, c));
+    const int64_t items = row_tiles * chunks;
+    const int64_t rounds = ceil_div(items, kCUs);
+    const int64_t cost = rounds * (c + kItemOverheadKeys);
+    if (cost < best_cost || (cost == best_cost && c > best_c)) {   // ties: larger chunk, fewer partials
+      best_cost = cost;
+      best_c = c;
+    }
+  }
+  return best_c;
+}
+
+int make_plan(const vamla_params* p, vamla_plan_info* out) {
+  const int st = check_shape(p);
+  if (st != VAMLA_OK) return st;
+  vamla_plan_info pl;
+  std::memset(&pl, 0, sizeof(pl));
+  const int64_t rows = (int64_t)p->max_tree * p->num_heads;
+  const int64_t row_tiles = ceil_div(rows, kRowTile);
+  const int64_t chunk = choose_chunk(p, row_tiles);
+  const int64_t max_chunks = std::max<int64_t>(1, ceil_div(p->max_prefix, chunk));
+  const int64_t items = (int64_t)p->batch * row_tiles * max_chunks;
+  if (items > (int64_t)INT32_MAX / 2) return VAMLA_ERR_UNSUPPORTED;
+  pl.chunk = (int32_t)chunk;
+  pl.row_tiles = (int32_t)row_tiles;
+  pl.max_chunks = (int32_t)max_chunks;
+  pl.grid_items = (int32_t)(ceil_div(items, 8) * 8);
+  const size_t item_o = (size_t)kD4 * kRowTile * 4 * sizeof(float);
+  const size_t item_l = (size_t)kRowTile * sizeof(float);
+  size_t off = 0;
+  pl.off_part_o = off;
+  off = align256(off + (size_t)items * item_o);
+  pl.off_part_lse = off;
+  off = align256(off + (size_t)items * item_l);
+  const size_t tiles = (size_t)p->batch * row_tiles;
+  pl.off_tail_o = off;
+  off = align256(off + tiles * item_o);
+  pl.off_tail_lse = off;
+  off = align256(off + tiles * item_l);
+  pl.workspace_bytes = off;
+  *out = pl;
+  return VAMLA_OK;
+}
+
+std::atomic<int> g_arch_state[64];   // 0 unknown, 1 gfx950, -1 other
+
+int check_arch() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return VAMLA_ERR_ARCH;
+  if (dev < 0 || dev >= 64) return VAMLA_ERR_ARCH;
+  int s = g_arch_state[dev].load(std::memory_order_relaxed);
+  if (s == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return VAMLA_ERR_ARCH;
+    s = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : -1;
+    g_arch_state[dev].store(s, std::memory_order_relaxed);
+  }
+  return s == 1 ? VAMLA_OK : VAMLA_ERR_ARCH;
+}
+
+int workspace_ok(const vamla_params* p, const vamla_plan_info& pl) {
+  if (!p->workspace || p->workspace_bytes < pl.workspace_bytes) return VAMLA_ERR_WORKSPACE;
+  if (((uintptr_t)p->workspace & 255) != 0) return VAMLA_ERR_WORKSPACE;
+  return VAMLA_OK;
+}
+
+float* ws_f(const vamla_params* p, size_t off) { return (float*)((char*)p->workspace + off); }
+
+int prefix_launch(const vamla_params* p, const vamla_plan_info& pl, const uint16_t* q, const uint16_t* pool,
+                  const int32_t* prefix_slot_idx, hipStream_t stream) {
+  if (p->total_prefix == 0 || p->max_prefix == 0) return VAMLA_OK;   // no prefix keys anywhere
+  PrefixArgs a;
+  a.q = q;
+  a.pool = pool;
+  a.prefix_slot = prefix_slot_idx;
+  a.cu_prefix = p->cu_prefix;
+  a.cu_tree = p->cu_tree;
+  a.part_o = ws_f(p, pl.off_part_o);
+  a.part_lse = ws_f(p, pl.off_part_lse);
+  a.num_heads = p->num_heads;
+  a.chunk = pl.chunk;
+  a.row_tiles = pl.row_tiles;
+  a.max_chunks = pl.max_chunks;
+  a.batch = p->batch;
+  a.grid_items = pl.grid_items;
+  a.scale_log2 = p->softmax_scale * 1.4426950408889634f;
+  return launch_prefix_splitkv(a, stream) == hipSuccess ? VAMLA_OK : VAMLA_ERR_LAUNCH;
+}
+
+int tail_launch(const vamla_params* p, const vamla_plan_info& pl, const uint16_t* q, const uint16_t* pool,
+                const int32_t* tree_slot_idx, const int32_t* parent, hipStream_t stream) {
+  TailArgs a;
+  a.q = q;
+  a.pool = pool;
+  a.tree_slot = tree_slot_idx;
+  a.parent = parent;
+  a.cu_tree = p->cu_tree;
+  a.tail_o = ws_f(p, pl.off_tail_o);
+  a.tail_lse = ws_f(p, pl.off_tail_lse);
+  a.num_heads = p->num_heads;
+  a.row_tiles = pl.row_tiles;
+  a.batch = p->batch;
+  a.total_tree = p->total_tree;
+  a.scale = p->softmax_scale;
+  return launch_tree_tail(a, stream) == hipSuccess ? VAMLA_OK : VAMLA_ERR_LAUNCH;
+}
+
+int merge_launch(const vamla_params* p, const vamla_plan_info& pl, uint16_t* out, float* lse, hipStream_t stream) {
+  MergeArgs a;
+  a.part_o = ws_f(p, pl.off_part_o);
+  a.part_lse = ws_f(p, pl.off_part_lse);
+  a.tail_o = ws_f(p, pl.off_tail_o);
+  a.tail_lse = ws_f(p, pl.off_tail_lse);
+  a.cu_prefix = p->cu_prefix;
+  a.cu_tree = p->cu_tree;
+  a.out = out;
+  a.lse = lse;
+  a.num_heads = p->num_heads;
+  a.chunk = pl.chunk;
+  a.row_tiles = pl.row_tiles;
+  // with no prefix keys anywhere the prefix pass never ran: merge the tail alone
+  a.max_chunks = pl.max_chunks;
+  a.batch = p->batch;
+  return launch_lse_merge(a, stream) == hipSuccess ? VAMLA_OK : VAMLA_ERR_LAUNCH;
+}
+
+// Common checks of every verify-family entry point; fills the plan.
+int prologue(const vamla_params* p, vamla_plan_info* pl) {
+  int st = make_plan(p, pl);
+  if (st != VAMLA_OK) return st;
+  if (!p->cu_prefix || !p->cu_tree) return VAMLA_ERR_INVALID_ARG;
+  st = workspace_ok(p, *pl);
+  if (st != VAMLA_OK) return st;
+  return check_arch();
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* vamla_status_string(int status) {
+  switch (status) {
+    case VAMLA_OK: return "ok";
+    case VAMLA_ERR_INVALID_ARG: return "invalid argument";
+    case VAMLA_ERR_UNSUPPORTED: return "unsupported shape";
+    case VAMLA_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+    case VAMLA_ERR_ARCH: return "current device is not gfx950";
+    case VAMLA_ERR_LAUNCH: return "kernel launch failed";
+    case VAMLA_ERR_INVALID_TREE: return "invalid tree (parent array)";
+    case VAMLA_ERR_INVALID_SLOT: return "slot index out of range";
+    case VAMLA_ERR_INVALID_LENGTHS: return "cumulative lengths inconsistent";
+    default: return "unknown status";
+  }
+}
+
+int vamla_plan(const vamla_params* p, vamla_plan_info* out) {
+  if (!out) return VAMLA_ERR_INVALID_ARG;
+  return make_plan(p, out);
+}
+
+int vamla_workspace_size(const vamla_params* p, size_t* bytes) {
+  if (!bytes) return VAMLA_ERR_INVALID_ARG;
+  vamla_plan_info pl;
+  const int st = make_plan(p, &pl);
+  if (st != VAMLA_OK) return st;
+  *bytes = pl.workspace_bytes;
+  return VAMLA_OK;
+}
+
+int vamla_validate(const vamla_params* p, const int32_t* h_parent, const int32_t* h_cu_tree,
+                   const int32_t* h_cu_prefix, const int32_t* h_prefix_slot_idx,
+                   const int32_t* h_tree_slot_idx) {
+  int st = check_shape(p);
+  if (st != VAMLA_OK) return st;
+  if (!h_parent || !h_cu_tree || !h_cu_prefix) return VAMLA_ERR_INVALID_ARG;
+  if (h_cu_tree[0] != 0 || h_cu_prefix[0] != 0) return VAMLA_ERR_INVALID_LENGTHS;
+  for (int b = 0; b < p->batch; ++b) {
+    const int64_t n = (int64_t)h_cu_tree[b + 1] - h_cu_tree[b];
+    const int64_t l = (int64_t)h_cu_prefix[b + 1] - h_cu_prefix[b];
+    if (n < 1 || n > p->max_tree) return VAMLA_ERR_INVALID_LENGTHS;
+    if (l < 0 || l > p->max_prefix) return VAMLA_ERR_INVALID_LENGTHS;
+  }
+  if (h_cu_tree[p->batch] != p->total_tree) return VAMLA_ERR_INVALID_LENGTHS;
+  if (h_cu_prefix[p->batch] != p->total_prefix) return VAMLA_ERR_INVALID_LENGTHS;
+  for (int b = 0; b < p->batch; ++b) {
+    const int t0 = h_cu_tree[b], n = h_cu_tree[b + 1] - t0;
+    if (h_parent[t0] != -1) return VAMLA_ERR_INVALID_TREE;
+    for (int i = 1; i < n; ++i) {
+      const int pa = h_parent[t0 + i];
+      if (pa < 0 || pa >= i) return VAMLA_ERR_INVALID_TREE;
+    }
+  }
+  if (h_prefix_slot_idx) {
+    for (int64_t i = 0; i < p->total_prefix; ++i)
+      if (h_prefix_slot_idx[i] < 0 || h_prefix_slot_idx[i] >= p->pool_slots) return VAMLA_ERR_INVALID_SLOT;
+  }
+  if (h_tree_slot_idx) {
+    for (int64_t i = 0; i < p->total_tree; ++i)
+      if (h_tree_slot_idx[i] < 0 || h_tree_slot_idx[i] >= p->pool_slots) return VAMLA_ERR_INVALID_SLOT;
+  }
+  return VAMLA_OK;
+}
+
+int verify_attn_mla(const vamla_params* p, const uint16_t* q, const uint16_t* kv_pool,
+                    const int32_t* prefix_slot_idx, const int32_t* tree_slot_idx, const int32_t* parent,
+                    uint16_t* out, float* lse, void* stream) {
+  vamla_plan_info pl;
+  int st = prologue(p, &pl);
+  if (st != VAMLA_OK) return st;
+  if (!q || !kv_pool || !tree_slot_idx || !parent || !out || !lse) return VAMLA_ERR_INVALID_ARG;
+  if (p->total_prefix > 0 && !prefix_slot_idx) return VAMLA_ERR_INVALID_ARG;
+  hipStream_t s = (hipStream_t)stream;
+  st = prefix_launch(p, pl, q, kv_pool, prefix_slot_idx, s);
+  if (st != VAMLA_OK) return st;
+  st = tail_launch(p, pl, q, kv_pool, tree_slot_idx, parent, s);
+  if (st != VAMLA_OK) return st;
+  return merge_launch(p, pl, out, lse, s);
+}
+
+int vamla_prefix_partials(const vamla_params* p, const uint16_t* q, const uint16_t* kv_pool,
+                          const int32_t* prefix_slot_idx, void* stream) {
+  vamla_plan_info pl;
+  int st = prologue(p, &pl);
+  if (st != VAMLA_OK) return st;
+  if (!q || !kv_pool) return VAMLA_ERR_INVALID_ARG;
+  if (p->total_prefix > 0 && !prefix_slot_idx) return VAMLA_ERR_INVALID_ARG;
+  return prefix_launch(p, pl, q, kv_pool, prefix_slot_idx, (hipStream_t)stream);
+}
+
+int vamla_tree_tail(const vamla_params* p, const uint16_t* q, const uint16_t* kv_pool,
+                    const int32_t* tree_slot_idx, const int32_t* parent, void* stream) {
+  vamla_plan_info pl;
+  int st = prologue(p, &pl);
+  if (st != VAMLA_OK) return st;
+  if (!q || !kv_pool || !tree_slot_idx || !parent) return VAMLA_ERR_INVALID_ARG;
+  return tail_launch(p, pl, q, kv_pool, tree_slot_idx, parent, (hipStream_t)stream);
+}
+
+int vamla_lse_merge(const vamla_params* p, uint16_t* out, float* lse, void* stream) {
+  vamla_plan_info pl;
+  int st = prologue(p, &pl);
+  if (st != VAMLA_OK) return st;
+  if (!out || !lse) return VAMLA_ERR_INVALID_ARG;
+  return merge_launch(p, pl, out, lse, (hipStream_t)stream);
+}
+
+int vamla_slot_gather(const uint16_t* kv_pool, const int32_t* idx, int64_t n, uint16_t* dst, void* stream) {
+  if (n < 0) return VAMLA_ERR_INVALID_ARG;
+  if (n == 0) return VAMLA_OK;
+  if (!kv_pool || !idx || !dst) return VAMLA_ERR_INVALID_ARG;
+  const int st = check_arch();
+  if (st != VAMLA_OK) return st;
+  return launch_slot_gather(kv_pool, idx, n, dst, (hipStream_t)stream) == hipSuccess ? VAMLA_OK
+                                                                                     : VAMLA_ERR_LAUNCH;
+}
+
+}  // extern "C"

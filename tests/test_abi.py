@@ -1,0 +1,178 @@
+"""CPU checks of the C ABI: the library loads, exports what include/vamla.h
+declares, and its host-only entry points (planning, workspace sizing,
+validation, argument checks) behave without touching a GPU."""
+
+import ctypes
+import math
+import os
+import re
+
+import numpy as np
+import pytest
+
+from speculative_decoding_tree_verify_amd import binding as vb
+from speculative_decoding_tree_verify_amd import inputs as gen
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "vamla.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(vb.LIB_PATH):
+        from speculative_decoding_tree_verify_amd import build
+        build.build()
+    return vb.lib()
+
+
+def header_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", src, flags=re.M)))
+
+
+def test_header_lists_the_entry_points():
+    fns = header_functions()
+    assert set(fns) == set(vb.EXPORTS)
+
+
+def test_every_declared_symbol_is_exported(L):
+    for name in header_functions():
+        assert hasattr(L, name), name
+
+
+def test_status_strings(L):
+    for code in vb.STATUS:
+        assert L.vamla_status_string(code)
+    assert L.vamla_status_string(0) == b"ok"
+
+
+def prob(k):
+    x = gen.config_inputs(k) if k in (1, 2) else None
+    table = {
+        1: vb.Problem(1, 16, 4096, gen.SOFTMAX_SCALE, 9, 9, 1024, 1024),
+        2: vb.Problem(1, 16, 32768, gen.SOFTMAX_SCALE, 9, 9, 8192, 8192),
+        3: vb.Problem(1, 16, 131072, gen.SOFTMAX_SCALE, 65, 65, 65536, 65536),
+        4: vb.Problem(1, 128, 1 << 20, gen.SOFTMAX_SCALE, 65, 65, 131072, 131072),
+        5: vb.Problem(8, 16, 1 << 21, gen.SOFTMAX_SCALE, 33, 264, 185000, 8 * 47500),
+    }
+    return table[k]
+
+
+@pytest.mark.parametrize("k", [1, 2, 3, 4, 5])
+def test_plan_covers_the_problem(L, k):
+    p = prob(k)
+    info = vb.plan(p)
+    assert info.chunk % 64 == 0 and info.chunk >= 64
+    assert info.row_tiles == math.ceil(p.max_tree * p.num_heads / 64)
+    assert info.max_chunks * info.chunk >= p.max_prefix
+    assert (info.max_chunks - 1) * info.chunk < max(p.max_prefix, 1)
+    assert info.grid_items % 8 == 0 and info.grid_items >= p.batch * info.row_tiles * info.max_chunks
+    items = p.batch * info.row_tiles * info.max_chunks
+    assert info.off_part_lse >= info.off_part_o + items * 128 * 64 * 16
+    assert info.off_tail_o >= info.off_part_lse + items * 64 * 4
+    assert info.workspace_bytes == vb.workspace_size(p)
+    for off in (info.off_part_o, info.off_part_lse, info.off_tail_o, info.off_tail_lse):
+        assert off % 256 == 0
+
+
+def test_plan_fills_the_chip_for_the_64k_config(L):
+    info = vb.plan(prob(3))
+    items = info.row_tiles * info.max_chunks
+    assert 200 <= items <= 256        # one round of work items over 256 CUs
+
+
+def test_explicit_chunk_is_kept(L):
+    p = prob(2)
+    p.chunk = 512
+    assert vb.plan(p).chunk == 512
+    p.chunk = 100                      # not a multiple of 64
+    with pytest.raises(vb.VamlaError) as e:
+        vb.plan(p)
+    assert e.value.status == -1
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("num_heads", 0, -2), ("num_heads", 129, -2), ("max_tree", 66, -2), ("max_tree", 0, -2),
+    ("batch", 0, -1), ("total_tree", 0, -1), ("max_prefix", -1, -1), ("pool_slots", 0, -1),
+])
+def test_plan_rejects_bad_shapes(L, field, value, code):
+    p = prob(1)
+    setattr(p, field, value)
+    with pytest.raises(vb.VamlaError) as e:
+        vb.plan(p)
+    assert e.value.status == code
+
+
+def test_plan_rejects_bad_dims(L):
+    p = prob(1).params()
+    p.d_qk = 512
+    info = vb.VamlaPlanInfo()
+    assert L.vamla_plan(ctypes.byref(p), ctypes.byref(info)) == -2
+    p = prob(1).params()
+    p.d_v = 576
+    assert L.vamla_plan(ctypes.byref(p), ctypes.byref(info)) == -2
+
+
+def test_verify_rejects_missing_workspace_before_touching_the_device(L):
+    p = prob(1).params(cu_prefix_ptr=16, cu_tree_ptr=16, workspace_ptr=0, workspace_bytes=0)
+    st = L.verify_attn_mla(ctypes.byref(p), 16, 16, 16, 16, 16, 16, 16, None)
+    assert st == -3
+    need = vb.workspace_size(prob(1))
+    p = prob(1).params(cu_prefix_ptr=16, cu_tree_ptr=16, workspace_ptr=256, workspace_bytes=need - 1)
+    assert L.verify_attn_mla(ctypes.byref(p), 16, 16, 16, 16, 16, 16, 16, None) == -3
+    p = prob(1).params(cu_prefix_ptr=16, cu_tree_ptr=16, workspace_ptr=128, workspace_bytes=need)
+    assert L.verify_attn_mla(ctypes.byref(p), 16, 16, 16, 16, 16, 16, 16, None) == -3   # misaligned
+    p = prob(1).params(cu_prefix_ptr=0, cu_tree_ptr=16, workspace_ptr=256, workspace_bytes=need)
+    assert L.verify_attn_mla(ctypes.byref(p), 16, 16, 16, 16, 16, 16, 16, None) == -1
+
+
+def test_slot_gather_empty_is_a_noop(L):
+    assert L.vamla_slot_gather(None, None, 0, None, None) == 0
+    assert L.vamla_slot_gather(None, None, -1, None, None) == -1
+
+
+def _valid_case():
+    x = gen.config_inputs(1)
+    p = vb.Problem.from_host(x.cu_prefix, x.cu_tree, 16, x.pool.shape[0], gen.SOFTMAX_SCALE)
+    return x, p
+
+
+def test_validate_accepts_generated_inputs(L):
+    x, p = _valid_case()
+    assert vb.validate(p, x.parent, x.cu_tree, x.cu_prefix, x.prefix_slot_idx, x.tree_slot_idx) == 0
+    x5 = gen.make_inputs([300, 0, 70], [gen.random_tree(5, np.random.default_rng(1)), np.array([-1]),
+                                        gen.chain_plus_branch()], 4, 4096, "scrambled", seed=3)
+    p5 = vb.Problem.from_host(x5.cu_prefix, x5.cu_tree, 4, 4096, 0.1)
+    assert vb.validate(p5, x5.parent, x5.cu_tree, x5.cu_prefix, x5.prefix_slot_idx, x5.tree_slot_idx) == 0
+
+
+def test_validate_catches_bad_trees(L):
+    x, p = _valid_case()
+    bad = x.parent.copy()
+    bad[3] = 3                        # self parent
+    assert vb.validate(p, bad, x.cu_tree, x.cu_prefix) == -6
+    bad = x.parent.copy()
+    bad[2] = 5                        # parent after child
+    assert vb.validate(p, bad, x.cu_tree, x.cu_prefix) == -6
+    bad = x.parent.copy()
+    bad[0] = 0                        # root must be -1
+    assert vb.validate(p, bad, x.cu_tree, x.cu_prefix) == -6
+    bad = x.parent.copy()
+    bad[4] = -1                       # second root
+    assert vb.validate(p, bad, x.cu_tree, x.cu_prefix) == -6
+
+
+def test_validate_catches_bad_slots_and_lengths(L):
+    x, p = _valid_case()
+    s = x.prefix_slot_idx.copy()
+    s[10] = x.pool.shape[0]
+    assert vb.validate(p, x.parent, x.cu_tree, x.cu_prefix, s, x.tree_slot_idx) == -7
+    t = x.tree_slot_idx.copy()
+    t[0] = -2
+    assert vb.validate(p, x.parent, x.cu_tree, x.cu_prefix, x.prefix_slot_idx, t) == -7
+    cp = x.cu_prefix.copy()
+    cp[1] += 1
+    assert vb.validate(p, x.parent, x.cu_tree, cp) == -8
+    p2 = vb.Problem(**{**p.__dict__, "max_tree": 8})
+    assert vb.validate(p2, x.parent, x.cu_tree, x.cu_prefix) == -8

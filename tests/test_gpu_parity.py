@@ -1,0 +1,225 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Tolerances: bf16 out within 1e-2 max-abs and within 1e-2 * max|out_ref|;
+fp32 lse within 1e-3; gather bit-exact.  Sizes span several key tiles, several
+row tiles and ragged tails; the five workload configurations run at full size
+(configs 4 and 5 on sampled heads / requests the oracle computes one by one).
+"""
+
+import numpy as np
+import pytest
+
+import oracle.verify_oracle as vo
+from speculative_decoding_tree_verify_amd import binding as vb
+from speculative_decoding_tree_verify_amd import inputs as gen
+
+from tests.gpu_util import assert_close_lse, assert_close_out, log, problem, run_verify, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def oracle_full(x, heads=None, requests=None):
+    return vo.verify(x.q, x.pool, x.prefix_slot_idx, x.tree_slot_idx, x.parent, x.cu_prefix, x.cu_tree,
+                     x.scale, heads=heads, requests=requests)
+
+
+def check(x, chunk=0, heads=None, requests=None, what=""):
+    log(f"[case] {what} B={x.batch} H={x.num_heads} T={x.total_tree} prefix={x.total_prefix} chunk={chunk}")
+    out, lse, _ = run_verify(x, chunk)
+    ro, rl = oracle_full(x, heads, requests)
+    sel = np.isfinite(rl)
+    assert sel.any()
+    assert_close_lse(lse[sel], rl[sel], what)
+    assert_close_out(out[sel], ro[sel], what)
+    return out, lse
+
+
+def small(prefix_lens, parents, H, seed, pool=None, mode="scrambled", std_q=0.1):
+    need = sum(prefix_lens) + sum(len(p) for p in parents)
+    return gen.make_inputs(prefix_lens, parents, H, pool or (need + 257), mode, seed, std_q=std_q)
+
+
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("chunk", [64, 128, 448, 0])
+def test_single_request_ragged(chunk):
+    rng = np.random.default_rng(1)
+    x = small([1000], [gen.random_tree(9, rng)], 3, seed=11)
+    check(x, chunk=chunk, what=f"ragged chunk={chunk}")
+
+
+def test_several_row_tiles():
+    rng = np.random.default_rng(2)
+    x = small([777], [gen.random_tree(9, rng)], 16, seed=12)        # 144 rows: tiles of 64, 64, 16
+    check(x, chunk=256, what="3 row tiles")
+
+
+def test_batch_varlen_with_empty_prefix():
+    rng = np.random.default_rng(3)
+    parents = [np.array([-1], np.int32), gen.random_tree(5, rng), gen.chain_plus_branch(), gen.random_tree(17, rng)]
+    x = small([0, 37, 500, 1300], parents, 8, seed=13)
+    check(x, chunk=192, what="batch varlen")
+
+
+def test_no_prefix_at_all():
+    rng = np.random.default_rng(4)
+    x = small([0, 0], [gen.random_tree(7, rng), gen.random_tree(3, rng)], 4, seed=14)
+    check(x, what="no prefix")
+
+
+def test_deepest_chain_and_widest_tree():
+    x = small([200], [np.arange(-1, 64, dtype=np.int32)], 2, seed=15)               # depth 64
+    check(x, chunk=64, what="chain of 65")
+    star = np.zeros(65, np.int32)
+    star[0] = -1
+    x = small([130], [star], 2, seed=16)                                              # 64 leaves
+    check(x, chunk=64, what="star of 65")
+
+
+def test_all_128_heads():
+    rng = np.random.default_rng(5)
+    x = small([300], [gen.random_tree(9, rng)], 128, seed=17)
+    check(x, chunk=128, what="H=128")
+
+
+def test_sharp_scores_move_the_reference():
+    rng = np.random.default_rng(6)
+    x = small([3000], [gen.random_tree(9, rng)], 4, seed=18, std_q=10.0)              # score sd ~ 1.7
+    check(x, chunk=1024, what="sharp scores")
+
+
+def test_reference_jump_mid_chunk():
+    # one prefix key deep inside a chunk gets a score far above everything
+    # before it, so the running reference max has to move mid-chunk
+    rng = np.random.default_rng(7)
+    x = small([2000], [gen.random_tree(5, rng)], 2, seed=19)
+    key = 1500
+    slot = x.prefix_slot_idx[key]
+    k = vo.bf16_bits_to_f64(x.pool[slot])
+    x.q[2, 1] = gen.f32_to_bf16_bits((k * 40.0).astype(np.float32))                  # score ~ 40*|k|^2*sigma
+    out, lse = check(x, chunk=2048, what="reference jump")
+    np.testing.assert_allclose(out[2, 1], k[:512], atol=2e-2)
+
+
+def test_config1():
+    check(gen.config_inputs(1), what="config 1")
+
+
+def test_config2_contiguous_and_scrambled_bit_identical():
+    a = gen.config_inputs(2, slot_mode="contiguous")
+    b = gen.config_inputs(2, slot_mode="scrambled")
+    oa, la = check(a, what="config 2 contiguous")
+    ob, lb = check(b, what="config 2 scrambled")
+    assert np.array_equal(oa, ob) and np.array_equal(la, lb)
+
+
+def test_config3_full():
+    x = gen.config_inputs(3)
+    check(x, what="config 3")
+
+
+def test_config4_sampled_heads():
+    x = gen.config_inputs(4)
+    check(x, heads=[0, 77, 127], what="config 4 heads 0,77,127")
+
+
+def test_config5_sampled_requests():
+    x = gen.config_inputs(5)
+    log(f"config 5 prefix lengths {[x.prefix_len(b) for b in range(8)]}")
+    check(x, requests=[0, 3, 7], heads=[0, 9, 15], what="config 5 requests 0,3,7")
+
+
+def test_determinism():
+    x = gen.config_inputs(1)
+    d = to_dev(x)
+    o1, l1, _ = run_verify(x, dev=d)
+    o2, l2, _ = run_verify(x, dev=d)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+# --- stage-level parity ----------------------------------------------------
+
+def test_stage_prefix_partials():
+    import torch
+    rng = np.random.default_rng(8)
+    x = small([700, 250], [gen.random_tree(9, rng), gen.random_tree(4, rng)], 8, seed=20)
+    p = problem(x, chunk=256)
+    d = to_dev(x)
+    ws = vb.Workspace(p)
+    vb.prefix_partials(p, d["q"], d["kv_pool"], d["prefix_slot_idx"], d["cu_prefix"], d["cu_tree"], ws)
+    torch.cuda.synchronize()
+    v = vb.workspace_views(p, ws)
+    part_o = v["part_o"].cpu().numpy()
+    part_lse = v["part_lse"].cpu().numpy()
+    for b in range(x.batch):
+        L, N, H = x.prefix_len(b), x.tree_len(b), x.num_heads
+        for s in range((L + 255) // 256):
+            ro, rl = vo.prefix_partial(x.q, x.pool, x.prefix_slot_idx, x.cu_prefix, x.cu_tree, b,
+                                       s * 256, min(L, (s + 1) * 256), x.scale)
+            ro = ro.reshape(N * H, 512)
+            rl = rl.reshape(N * H)
+            rows = np.arange(N * H)
+            tile, rit = rows // 64, rows % 64
+            got_l = part_lse[b, tile, s, rit]
+            got_o = part_o[b, tile, s].reshape(len(rows), 128, 64, 4)[np.arange(len(rows)), :, rit, :].reshape(len(rows), 512)
+            assert_close_lse(got_l, rl, f"partial b={b} s={s}")
+            np.testing.assert_allclose(got_o, ro, atol=2e-3 * np.abs(ro).max() + 1e-6)
+
+
+def test_stage_tree_tail():
+    import torch
+    rng = np.random.default_rng(9)
+    parents = [gen.random_tree(12, rng), gen.bounded_tree(33, rng), np.array([-1], np.int32)]
+    x = small([10, 20, 30], parents, 6, seed=21)
+    p = problem(x)
+    d = to_dev(x)
+    ws = vb.Workspace(p)
+    vb.tree_tail(p, d["q"], d["kv_pool"], d["tree_slot_idx"], d["parent"], d["cu_prefix"], d["cu_tree"], ws)
+    torch.cuda.synchronize()
+    v = vb.workspace_views(p, ws)
+    tail_o = v["tail_o"].cpu().numpy()
+    tail_l = v["tail_lse"].cpu().numpy()
+    for b in range(x.batch):
+        N, H = x.tree_len(b), x.num_heads
+        ro, rl = vo.tree_partial(x.q, x.pool, x.tree_slot_idx, x.parent, x.cu_tree, b, x.scale)
+        rows = np.arange(N * H)
+        tile, rit = rows // 64, rows % 64
+        got_l = tail_l[b, tile, rit]
+        got_o = np.stack([tail_o[b, tile[i], :, rit[i], :].reshape(512) for i in rows])
+        np.testing.assert_allclose(got_l, rl.reshape(-1), atol=1e-4)
+        np.testing.assert_allclose(got_o, ro.reshape(N * H, 512), atol=1e-4)
+
+
+def test_slot_gather_bit_exact():
+    import torch
+    x = gen.config_inputs(2, slot_mode="scrambled")
+    d = to_dev(x)
+    idx = d["prefix_slot_idx"]
+    dst = vb.slot_gather(d["kv_pool"], idx)
+    torch.cuda.synchronize()
+    got = dst.view(torch.int16).cpu().numpy().view(np.uint16)
+    assert np.array_equal(got, vo.gather_rows(x.pool, x.prefix_slot_idx))
+    # ragged count, repeated slots
+    idx2 = torch.tensor([5, 5, 1, 32767, 9, 9, 9], dtype=torch.int32, device="cuda")
+    dst2 = vb.slot_gather(d["kv_pool"], idx2)
+    torch.cuda.synchronize()
+    assert np.array_equal(dst2.view(torch.int16).cpu().numpy().view(np.uint16),
+                          vo.gather_rows(x.pool, [5, 5, 1, 32767, 9, 9, 9]))
+
+
+def test_defragmented_pool_gives_identical_result():
+    import torch
+    x = gen.config_inputs(2, slot_mode="scrambled")
+    d = to_dev(x)
+    o1, l1, _ = run_verify(x, dev=d)
+    # compact prefix then tree rows into slots 1..n of a fresh pool via the gather kernel
+    order = torch.cat([d["prefix_slot_idx"], d["tree_slot_idx"]])
+    rows = vb.slot_gather(d["kv_pool"], order)
+    pool2 = torch.zeros_like(d["kv_pool"])
+    pool2[1:1 + rows.shape[0]] = rows
+    n = x.total_prefix
+    d2 = dict(d, kv_pool=pool2,
+              prefix_slot_idx=torch.arange(1, n + 1, dtype=torch.int32, device="cuda"),
+              tree_slot_idx=torch.arange(n + 1, n + 1 + x.total_tree, dtype=torch.int32, device="cuda"))
+    o2, l2, _ = run_verify(x, dev=d2)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
