@@ -1,0 +1,248 @@
+#!/usr/bin/env python3
+"""Benchmark of DDTree verify attention for MLA on one MI355X.
+
+One step = one verify_attn_mla call (prefix split-KV pass + masked tree tail +
+LSE merge) over the 64k-prefix / 65-node workload: batch 1, 16 heads, 576/512
+dims, a depth-8 tree with branching <= 4, prefix rows scattered over a
+131072-slot bf16 pool.  Inputs are seeded synthetic data, resident in HBM
+before timing.  Several copies of the pool are rotated between steps so each
+step reads its KV rows from HBM rather than the 256 MB Infinity Cache.
+
+Prints ONE JSON line (stdout):
+  value        effective KV-read bandwidth = unique KV bytes / step time (GB/s)
+  roofline     the prefix kernel (the dominant one) against the bf16 MFMA peak,
+               timed with HIP events on the stream it runs on
+  cpu_baseline the fp64 oracle on host cores, same workload (test infrastructure)
+Details go to stderr.
+
+  python bench.py [--steps K] [--warmup W] [--config 1..5] [--no-cpu]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from speculative_decoding_tree_verify_amd import binding as vb  # noqa: E402
+from speculative_decoding_tree_verify_amd import inputs as gen  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
+KV_ROW_BYTES = 576 * 2
+FLOPS_PER_ROW_KEY = 2 * (576 + 512)
+POOL_ROTATION_BYTES = 768 << 20   # > 3x the Infinity Cache
+
+
+def err(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def workload_name(k: int) -> str:
+    return gen.CONFIG_NAMES[k]
+
+
+def algorithmic(x: gen.VerifyInputs):
+    """Work the method must do per step (not the implementation's traffic)."""
+    H = x.num_heads
+    kv_rows = x.total_prefix + x.total_tree
+    prefix_flops = 0
+    tail_flops = 0
+    for b in range(x.batch):
+        N, L = x.tree_len(b), x.prefix_len(b)
+        prefix_flops += H * N * L * FLOPS_PER_ROW_KEY
+        par = x.parent[x.cu_tree[b]:x.cu_tree[b + 1]]
+        depth = gen.tree_depths(par)
+        tail_flops += H * int((depth + 1).sum()) * FLOPS_PER_ROW_KEY
+    T = x.total_tree
+    io_bytes = T * H * (KV_ROW_BYTES + 512 * 2 + 4)
+    return dict(kv_bytes=kv_rows * KV_ROW_BYTES, prefix_flops=prefix_flops, tail_flops=tail_flops,
+                io_bytes=io_bytes)
+
+
+def time_events(fn, iters: int) -> float:
+    """Average ms per call of fn (launches on torch's current stream)."""
+    import torch
+    s = torch.cuda.Event(enable_timing=True)
+    e = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    s.record()
+    for i in range(iters):
+        fn(i)
+    e.record()
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) / iters
+
+
+def cpu_baseline(x: gen.VerifyInputs, kv_bytes: int, budget_s: float = 20.0):
+    """Time the fp64 oracle on the host: the whole verify step, repeated while
+    the budget lasts (at least once)."""
+    import oracle.verify_oracle as vo
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:
+        cores = os.cpu_count() or 1
+    times = []
+    t_end = time.perf_counter() + budget_s
+    while True:
+        t0 = time.perf_counter()
+        vo.verify(x.q, x.pool, x.prefix_slot_idx, x.tree_slot_idx, x.parent, x.cu_prefix, x.cu_tree, x.scale)
+        times.append(time.perf_counter() - t0)
+        if time.perf_counter() + times[-1] > t_end or len(times) >= 5:
+            break
+    t = float(np.median(times))
+    return {"value": round(kv_bytes / t / 1e9, 4), "unit": "GB/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"full verify step of the same workload (all heads and nodes), fp64 numpy, "
+                      f"{len(times)} run(s), median {t * 1e3:.1f} ms/step",
+            "ms_per_step": round(t * 1e3, 3)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", type=int, default=3)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="also run a plain 512 MiB device copy (counter calibration under rocprofv3 --pmc)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the verify path runs on a single MI355X and has no multi-GPU mode "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    vb.lib()   # fail loudly if the HIP library is missing
+
+    t0 = time.perf_counter()
+    x = gen.config_inputs(args.config)
+    err(f"[bench] workload: {workload_name(args.config)}  (inputs generated in {time.perf_counter() - t0:.1f} s)")
+    alg = algorithmic(x)
+    prob = vb.Problem.from_host(x.cu_prefix, x.cu_tree, x.num_heads, x.pool.shape[0], x.scale)
+    info = vb.plan(prob)
+    err(f"[bench] plan: chunk={info.chunk} row_tiles={info.row_tiles} chunks={info.max_chunks} "
+        f"grid={info.grid_items} workspace={info.workspace_bytes / 1e6:.1f} MB")
+
+    dev = "cuda"
+    bf = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+    i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
+    q = bf(x.q)
+    pool_bytes = x.pool.nbytes
+    n_copies = max(1, min(8, -(-POOL_ROTATION_BYTES // pool_bytes)))
+    pools = [bf(x.pool)]
+    for _ in range(n_copies - 1):
+        pools.append(pools[0].clone())
+    pre, tre, par = i32(x.prefix_slot_idx), i32(x.tree_slot_idx), i32(x.parent)
+    cup, cut = i32(x.cu_prefix), i32(x.cu_tree)
+    ws = vb.Workspace(prob)
+    out = torch.empty((x.total_tree, x.num_heads, 512), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((x.total_tree, x.num_heads), dtype=torch.float32, device=dev)
+    err(f"[bench] {n_copies} pool copies of {pool_bytes / 1e6:.1f} MB rotated between steps")
+
+    def step(i):
+        vb.verify_attn_mla(prob, q, pools[i % n_copies], pre, tre, par, cup, cut, ws=ws, out=out, lse=lse)
+
+    def prefix_only(i):
+        vb.prefix_partials(prob, q, pools[i % n_copies], pre, cup, cut, ws)
+
+    def tail_only(i):
+        vb.tree_tail(prob, q, pools[i % n_copies], tre, par, cup, cut, ws)
+
+    def merge_only(i):
+        vb.lse_merge(prob, cup, cut, ws, out, lse)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # --- timed region: exactly K steps ---
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+    value = alg["kv_bytes"] / (ms_per_step * 1e-3) / 1e9
+
+    # --- per-kernel durations (HIP events on the launch stream) ---
+    iters = max(20, min(args.steps, 200))
+    ms_prefix = time_events(prefix_only, iters)
+    ms_tail = time_events(tail_only, iters)
+    ms_merge = time_events(merge_only, iters)
+    ms_step_ev = time_events(step, iters)
+    achieved = alg["prefix_flops"] / (ms_prefix * 1e-3) / 1e12
+    err(f"[bench] step {ms_per_step * 1e3:.1f} us (wall), {ms_step_ev * 1e3:.1f} us (events); "
+        f"prefix {ms_prefix * 1e3:.1f} us, tail {ms_tail * 1e3:.1f} us, merge {ms_merge * 1e3:.1f} us")
+    err(f"[bench] prefix kernel {achieved:.1f} TFLOP/s = {achieved / MFMA_BF16_PEAK_TFLOPS * 100:.1f}% of bf16 "
+        f"MFMA peak; effective KV {value:.1f} GB/s = {value / HBM_PEAK_GBS * 100:.2f}% of HBM peak")
+    t_mfma = (alg["prefix_flops"] + alg["tail_flops"]) / (MFMA_BF16_PEAK_TFLOPS * 1e12)
+    t_hbm = (alg["kv_bytes"] + alg["io_bytes"]) / (HBM_PEAK_GBS * 1e9)
+    err(f"[bench] roofline bounds per step: MFMA {t_mfma * 1e6:.1f} us, HBM {t_hbm * 1e6:.1f} us; "
+        f"fraction of binding roofline {max(t_mfma, t_hbm) / (ms_per_step * 1e-3):.3f}")
+
+    if args.calib_copy:
+        a = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        err("[bench] calibration copy: 3 x 512 MiB device-to-device")
+
+    cpu = None
+    if not args.no_cpu:
+        del pools
+        cpu = cpu_baseline(x, alg["kv_bytes"])
+        err(f"[bench] cpu oracle: {cpu['ms_per_step']:.1f} ms/step on {cpu['cores']} threads")
+
+    rec = {
+        "metric": "effective KV-read GB/s (% HBM peak) + us per verify step, 64k prefix, 65 nodes",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "strong",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": workload_name(args.config),
+            "batch": x.batch, "heads": x.num_heads, "prefix": x.total_prefix, "tree_nodes": x.total_tree,
+            "pool_slots": int(x.pool.shape[0]), "kv_bytes": alg["kv_bytes"],
+            "us_per_step": round(ms_per_step * 1e3, 2),
+            "pct_hbm_peak": round(value / HBM_PEAK_GBS * 100, 3),
+            "kernel_us": {"prefix_splitkv": round(ms_prefix * 1e3, 2), "tree_tail": round(ms_tail * 1e3, 2),
+                          "lse_merge": round(ms_merge * 1e3, 2)},
+            "binding_roofline_fraction": round(max(t_mfma, t_hbm) / (ms_per_step * 1e-3), 4),
+        },
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": MFMA_BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+            "traffic": None,
+        },
+        "cpu_baseline": ({k: v for k, v in cpu.items() if k != "ms_per_step"} if cpu else None),
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()
