@@ -10,35 +10,45 @@
 //
 // Work item = (request b, row tile of 64 query rows, chunk s); one 256-thread
 // workgroup (4 waves) per item.  All H*N query rows of a request read every
-// prefix key, so the pass is a dense contraction and runs on MFMA.
+// prefix key, so the pass is a dense contraction and runs on MFMA
+// (v_mfma_f32_32x32x16_bf16, fp32 accumulation).
 //
-// Waves form two pairs.  Pair p owns query rows [32p, 32p+32) of the tile; the
-// two waves of a pair split the work of each 64-key tile:
-//   * QK: wave (p, h) computes S^T = K Q^T for keys [32h, 32h+32) of the tile
-//     on v_mfma_f32_32x32x16_bf16 (A = K rows from LDS via ds_read_b128, B = the
-//     pair's 32 query rows, held in VGPRs for the whole item).  In the 32x32
-//     accumulator layout each lane owns one query row.
-//   * softmax: P = exp2(S*scale*log2e - m) in bf16, written to LDS so the
-//     partner can read it as its own MFMA operand, lane for lane.
-//   * PV: wave (p, h) accumulates O^T += V^T P^T for output columns
-//     [256h, 256h+256) over all 64 keys (A = V^T read from the same LDS tile by
-//     the transposing ds_read_b64_tr_b16, B = own P and the partner's P).
-// A wave thus holds 32x576 Q (144 VGPRs) and a 32x256 accumulator (128), which
-// leaves the compiler room; LDS bytes per MFMA flop equal those of one wave
-// doing all 512 columns.
+// Waves form two pairs; pair p owns query rows [32p, 32p+32) of the tile and
+// wave (p, h) of the pair:
+//   * QK: holds half of the 576 query columns (latent [256h, 256h+256) and
+//     rope [32h, 32h+32)) in VGPRs and computes the partial scores S^T = K Q^T
+//     over that half for all 64 keys of the tile (A = K from LDS, B = Q).  In
+//     the 32x32 accumulator layout each lane owns one query row.
+//   * exchange: keeps the partial of key block h, sends the other block to its
+//     partner through LDS; adding the partner's half gives the full scores of
+//     keys [32h, 32h+32).
+//   * softmax: P = exp2(S*scale*log2e - m) in bf16 for those 32 keys, sent to
+//     the partner lane for lane (it is the partner's MFMA operand as well).
+//   * PV: O^T += V^T P^T for output columns [256h, 256h+256) over all 64 keys
+//     (A = V^T read from the same LDS tile by ds_read_b64_tr_b16, B = P).
+// Per wave: Q 72 VGPRs, a 32x256 fp32 accumulator (128), so the compiler has
+// room to keep the LDS operand reads several MFMAs ahead.
 //
-// Gather: the 1152-byte pool row of each key is fetched as 72 sixteen-byte
-// pieces with global_load_lds_dwordx4 (straight into LDS, no VGPR staging).
-// LDS tile layout is piece-major: byte(key, c) = (c*64 + (key ^ 8*(c&1)))*16,
-// which keeps both the ds_read_b128 (QK) and ds_read_b64_tr_b16 (PV) patterns
+// Gather: global_load_lds_dwordx4 moves 16 bytes per lane straight into LDS
+// (no VGPR staging).  Per key, one instruction fetches the 1 KB latent part of
+// its pool row (8 cache lines) and one 8-lane instruction the 128-byte rope
+// part; the slot of each key is a scalar, loaded one tile ahead.  LDS tile
+// layout (72 KB per 64 keys):
+//   latent: key k at k*1024, 16-byte piece c at slot c ^ g(k),
+//           g(k) = ((k & 7) << 1) | ((k >> 3) & 1)
+//   rope:   key k at 64 KB + k*128, piece c at slot c ^ ((k >> 1) & 7)
+// Lane-linear DMA writes pick the piece each lane loads, so the swizzle is
+// free; it keeps the ds_read_b128 (QK) and ds_read_b64_tr_b16 (PV) patterns
 // free of bank conflicts.  Tiles are double-buffered: the gather of tile t+1
 // runs under the math of tile t.
 //
-// Softmax reference: each row keeps a reference max m.  It only moves when a
-// tile's max exceeds it by more than kSlack (log2 units); until then
-// exp2(s - m) <= 2^kSlack, well inside bf16/fp32 range, and the O rescale stays
-// off the common path.  Moving it is a workgroup-uniform decision, taken after
-// the P exchange, with P recomputed from the kept scores.
+// Softmax reference: each row keeps a reference m (log2 units) instead of a
+// running max, so the accumulator is never rescaled and stays in AGPRs.  The
+// first tile sets m to the pair's tile max.  While every score stays within
+// kSlack of m, exp2(s - m) <= 2^kSlack, far inside bf16/fp32 range.  A tile
+// that breaks this (rare) makes the whole workgroup restart its chunk with
+// m raised to that tile's max plus kSlack of headroom; m only grows, by more
+// than kSlack per restart, so restarts are few and the result is the same.
 
 #include "kernels.h"
 
@@ -53,22 +63,34 @@ typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 constexpr float kLn2 = 0.69314718055994530942f;
-constexpr float kSlack = 16.0f;     // reference max may lag the true max by this much (log2 units)
-constexpr float kClamp = 24.0f;     // P exponent cap for the speculative pass
+constexpr float kSlack = 16.0f;     // scores may exceed the reference by this much (log2 units)
+constexpr int kRopeBase = 64 * 1024;
+constexpr int kPre = 4;             // LDS operand reads in flight ahead of their MFMA
 
-// LDS: two key tiles + exchange area
+// Exchange area: per wave, 64 bytes per lane.  Wave w writes its partial
+// scores for the partner's key block into v[w]; the partner reads them and
+// then reuses that same slot to send back its P operands and tile max.
 struct __attribute__((aligned(16))) Xchg {
-  // [wave][slot][lane]: slots 0, 1 = the two P operands of the wave's keys;
-  // slot 2 = (tile max of the lane's row, move flag, -, -) as four floats
-  bf16x8 p[4][3][64];
-  float lsum[4][64];                // [wave][lane] final row-sum shares
+  float4 v[4][4][64];               // [wave][16-byte part][lane], 16 KB
 };
+
+__device__ __forceinline__ int swz_latent(int k) { return ((k & 7) << 1) | ((k >> 3) & 1); }
+__device__ __forceinline__ int swz_rope(int k) { return (k >> 1) & 7; }
 
 // Workgroup barrier that waits only for this wave's LDS operations.  A fence
 // would also wait for the in-flight gathers (LDS DMA counts as LDS stores),
 // which must keep running under the math.
 __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// base ^ c, computed where it is used (an opaque xor keeps the compiler from
+// hoisting every variant of a swizzled base into its own register)
+__device__ __forceinline__ int xor_at_use(int base, int c) {
+  if (c == 0) return base;
+  int r;
+  asm volatile("v_xor_b32 %0, %2, %1" : "=v"(r) : "v"(base), "i"(c));   // literal must be src0
+  return r;
 }
 
 __device__ __forceinline__ bf16x8 tr_pair(const uint8_t* base, int off1, int off2) {
@@ -78,18 +100,36 @@ __device__ __forceinline__ bf16x8 tr_pair(const uint8_t* base, int off1, int off
   return __builtin_bit_cast(bf16x8, v);
 }
 
-// Issue this wave's 18 pieces (c = w, w+4, ..., w+68) of one key tile.
-__device__ __forceinline__ void gather_tile(const uint16_t* rowp, uint8_t* lds, int w) {
+// Part `part` (keys [16w + 4*part, 16w + 4*part + 4)) of this wave's share of
+// one key tile; `sl` holds the slots of the wave's 16 keys.
+__device__ __forceinline__ void gather_part(const uint16_t* pool, const uint32_t (&sl)[16], uint8_t* lds, int w,
+                                            int lane, int part) {
+  const int lane16 = lane << 4;
 #pragma unroll
-  for (int j = 0; j < kChunks16 / 4; ++j) {
-    const int c = w + 4 * j;
-    __builtin_amdgcn_global_load_lds((const void*)(rowp + c * 8), (lds_void*)(lds + c * 1024), 16, 0, 0);
+  for (int i = 4 * part; i < 4 * part + 4; ++i) {
+    const uint8_t* row = (const uint8_t*)(pool + (size_t)sl[i] * kDqk);
+    const int k = 16 * w + i;
+    __builtin_amdgcn_global_load_lds((const void*)(row + (uint32_t)xor_at_use(lane16, swz_latent(i) << 4)),
+                                     (lds_void*)(lds + k * 1024), 16, 0, 0);
+    if (lane < 8)
+      __builtin_amdgcn_global_load_lds(
+          (const void*)(row + 1024 + (uint32_t)xor_at_use(lane16, swz_rope(i) << 4)),
+          (lds_void*)(lds + kRopeBase + k * 128), 16, 0, 0);
   }
+}
+
+__device__ __forceinline__ void gather_tile(const uint16_t* pool, const uint32_t (&sl)[16], uint8_t* lds, int w,
+                                            int lane) {
+#pragma unroll
+  for (int part = 0; part < 4; ++part) gather_part(pool, sl, lds, w, lane, part);
 }
 
 struct Lane {
   int w, pr, hf, hl, l32, lane;
-  int qk_off, trb1, trb2;
+  // Swizzled LDS addresses are written base ^ (step-dependent bits) + immediate:
+  int qk_lat;        // latent: key*1024 + 512*hf | ((hl ^ g(key)) << 4); step s: ^ 32*(s&7), + 256*(s>>3)
+  int qk_rope;       // rope: 64K + key*128 | ((4*hf ^ hl ^ h(key)) << 4); rope step r: ^ 32*r
+  int pv[2];         // PV transposed reads, key group sec: column block d: ^ 64*(d&3), + 256*(d>>2)
 };
 
 struct RowState {
@@ -97,94 +137,133 @@ struct RowState {
   float l;   // this lane's share of the row sum
 };
 
-__device__ __forceinline__ void pack_p(const f32x16& v, float m, bf16x8 (&pb)[2], float& lsum, float cap) {
+// K fragment of QK step s for key block kb: this wave's d-half, pieces
+// 2s and 2s+1 of it (lane half hl takes 2s+hl).
+__device__ __forceinline__ bf16x8 kfrag(const uint8_t* lds, const Lane& ln, int kb, int s) {
+  if (s < 16) return *(const bf16x8*)(lds + xor_at_use(ln.qk_lat, 32 * (s & 7)) + (s >> 3) * 256 + kb * 32768);
+  return *(const bf16x8*)(lds + xor_at_use(ln.qk_rope, 32 * (s - 16)) + kb * 4096);
+}
+
+// P = exp2(s*scale - m) in bf16 for this lane's 16 raw scores; lsum += sum P.
+__device__ __forceinline__ void pack_p(const f32x16& v, float scale, float m, bf16x8 (&pb)[2], float& lsum) {
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const float p = __builtin_amdgcn_exp2f(fminf(v[half * 8 + e] - m, cap));
+      const float p = __builtin_amdgcn_exp2f(fmaf(v[half * 8 + e], scale, -m));
       lsum += p;
       pb[half][e] = (__bf16)p;
     }
   }
 }
 
-// One staged 64-key tile for this wave.
-__device__ __forceinline__ void tile_math(const uint8_t* lds, Xchg& x, const bf16x8 (&qf)[36],
+// One staged 64-key tile for this wave.  Returns true when the workgroup
+// must restart its chunk (this tile was not accumulated).
+__device__ __forceinline__ bool tile_math(const uint8_t* lds, Xchg& x, const bf16x8 (&qf)[18],
                                           f32x16 (&o)[8], RowState& st, int nvalid, float scale_log2,
                                           const Lane& ln) {
-  // S^T for this wave's 32 keys
-  f32x16 v = {};
+  // partial S^T over this wave's d-half, key blocks 0 and 1 interleaved so
+  // consecutive MFMAs never depend on each other
+  f32x16 sp0 = {}, sp1 = {};
+  {
+    bf16x8 kf[kPre];
 #pragma unroll
-  for (int s = 0; s < 36; ++s) {
-    const bf16x8 a = *(const bf16x8*)(lds + ln.qk_off + s * 2048);
-    v = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], v, 0, 0, 0);
-  }
-  // lane holds keys 32*hf + 8*(r/4) + 4*hl + r%4 of row l32
-  float mt = -INFINITY;
+    for (int i = 0; i < kPre; ++i) kf[i] = kfrag(lds, ln, i & 1, i >> 1);
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    float t = v[r] * scale_log2;
-    if (32 * ln.hf + 8 * (r >> 2) + 4 * ln.hl + (r & 3) >= nvalid) t = -INFINITY;
-    v[r] = t;
-    mt = fmaxf(mt, t);
+    for (int i = 0; i < 36; ++i) {
+      const int kb = i & 1, s = i >> 1;
+      const bf16x8 cur = kf[i % kPre];
+      if (i + kPre < 36) kf[i % kPre] = kfrag(lds, ln, (i + kPre) & 1, (i + kPre) >> 1);
+      if (kb) sp1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur, qf[s], sp1, 0, 0, 0);
+      else sp0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur, qf[s], sp0, 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
-  mt = fmaxf(mt, __shfl_xor(mt, 32));
-  // speculative P against the current reference
+  // send the partner its key block, take ours
+  const f32x16 give = ln.hf ? sp0 : sp1;
+  f32x16 v = ln.hf ? sp1 : sp0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    x.v[ln.w][q][ln.lane] = make_float4(give[4 * q], give[4 * q + 1], give[4 * q + 2], give[4 * q + 3]);
+  lds_barrier();
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const float4 t = x.v[ln.w ^ 1][q][ln.lane];
+    v[4 * q] += t.x;
+    v[4 * q + 1] += t.y;
+    v[4 * q + 2] += t.z;
+    v[4 * q + 3] += t.w;
+  }
+  // lane holds keys 32*hf + 8*(r/4) + 4*hl + r%4 of row l32 (raw scores)
+  if (nvalid < kKeyTile) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      if (32 * ln.hf + 8 * (r >> 2) + 4 * ln.hl + (r & 3) >= nvalid) v[r] = -INFINITY;
+  }
+  float mt = v[0];
+#pragma unroll
+  for (int r = 1; r < 16; ++r) mt = fmaxf(mt, v[r]);
+  mt = fmaxf(mt, __shfl_xor(mt, 32)) * scale_log2;          // row max over my 32 keys, log2 units
+  // P against the current reference, sent in the slot just read
   float lsum = 0.f;
   bf16x8 pb[2];
-  pack_p(v, st.m, pb, lsum, kClamp);
-  x.p[ln.w][0][ln.lane] = pb[0];
-  x.p[ln.w][1][ln.lane] = pb[1];
+  pack_p(v, scale_log2, st.m, pb, lsum);
   const float want = __any(mt > st.m + kSlack) ? 1.f : 0.f;
-  x.p[ln.w][2][ln.lane] = __builtin_bit_cast(bf16x8, make_float4(mt, want, 0.f, 0.f));
+  x.v[ln.w ^ 1][0][ln.lane] = __builtin_bit_cast(float4, pb[0]);
+  x.v[ln.w ^ 1][1][ln.lane] = __builtin_bit_cast(float4, pb[1]);
+  x.v[ln.w ^ 1][2][ln.lane] = make_float4(mt, want, 0.f, 0.f);
   lds_barrier();
-  auto aux = [&](int w, int l) { return __builtin_bit_cast(float4, x.p[w][2][l]); };
-  // each writer stored its wave-uniform flag in every lane, so read at own lane
-  const float any_flag = aux(0, ln.lane).y + aux(1, ln.lane).y + aux(2, ln.lane).y + aux(3, ln.lane).y;
+  // every wave stored its wave-uniform flag in all lanes, so read at own lane
+  const float any_flag = x.v[0][2][ln.lane].y + x.v[1][2][ln.lane].y + x.v[2][2][ln.lane].y + x.v[3][2][ln.lane].y;
   if (__builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, any_flag)) != 0) {
-    // move the pair's reference to the pair's tile max (rare: first tile, or a
-    // jump of more than kSlack); both waves of the pair compute the same m_new
-    const float m_new = fmaxf(st.m, fmaxf(mt, aux(ln.w ^ 1, ln.lane).x));
-    const float alpha = __builtin_amdgcn_exp2f(st.m - m_new);
-    st.m = m_new;
-    st.l *= alpha;
-#pragma unroll
-    for (int d = 0; d < 8; ++d) o[d] *= alpha;
+    // pair max of this tile (both waves of the pair compute the same value)
+    const float mp = fmaxf(mt, x.v[ln.w][2][ln.lane].x);
+    if (__builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, st.m)) != __builtin_bit_cast(int, -INFINITY)) {
+      // a score ran past the reference: restart the chunk with headroom
+      st.m = fmaxf(st.m, mp) + kSlack;
+      return true;
+    }
+    // first tile of the chunk: take the pair max as the reference; the
+    // accumulators are still zero, so only P is recomputed
+    st.m = mp;
     lsum = 0.f;
-    pack_p(v, st.m, pb, lsum, INFINITY);
+    pack_p(v, scale_log2, st.m, pb, lsum);
     lds_barrier();
-    x.p[ln.w][0][ln.lane] = pb[0];
-    x.p[ln.w][1][ln.lane] = pb[1];
+    x.v[ln.w ^ 1][0][ln.lane] = __builtin_bit_cast(float4, pb[0]);
+    x.v[ln.w ^ 1][1][ln.lane] = __builtin_bit_cast(float4, pb[1]);
     lds_barrier();
   }
   st.l += lsum;
-  const bf16x8 pq0 = x.p[ln.w ^ 1][0][ln.lane];
-  const bf16x8 pq1 = x.p[ln.w ^ 1][1][ln.lane];
-  // O^T += V^T P^T for this wave's 256 output columns over all 64 keys
+  const bf16x8 pq0 = __builtin_bit_cast(bf16x8, x.v[ln.w][0][ln.lane]);
+  const bf16x8 pq1 = __builtin_bit_cast(bf16x8, x.v[ln.w][1][ln.lane]);
+  // O^T += V^T P^T for this wave's 256 output columns over all 64 keys;
+  // the eight column blocks are interleaved so consecutive MFMAs are independent
+  {
+    auto vfrag = [&](int i) {   // i = (kb*2 + half)*8 + j
+      const int j = i & 7, kb = i >> 4, half = (i >> 3) & 1;
+      const int off = (kb * 32 + half * 16) * 1024 + (j >> 2) * 256;
+      return tr_pair(lds, xor_at_use(ln.pv[0], 64 * (j & 3)) + off, xor_at_use(ln.pv[1], 64 * (j & 3)) + off);
+    };
+    bf16x8 vf[kPre];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int dblk = 8 * ln.hf + j;
+    for (int i = 0; i < kPre; ++i) vf[i] = vfrag(i);
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        const int off = dblk * 4096 + kb * 512 + half * 256;
-        const bf16x8 a = tr_pair(lds, ln.trb1 + off, ln.trb2 + off);
-        const bf16x8 bop = (kb == ln.hf) ? pb[half] : (half ? pq1 : pq0);
-        o[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bop, o[j], 0, 0, 0);
-      }
+    for (int i = 0; i < 32; ++i) {
+      const int j = i & 7, kb = i >> 4, half = (i >> 3) & 1;
+      const bf16x8 cur = vf[i % kPre];
+      if (i + kPre < 32) vf[i % kPre] = vfrag(i + kPre);
+      const bf16x8 bop = (kb == ln.hf) ? pb[half] : (half ? pq1 : pq0);
+      o[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur, bop, o[j], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
+  return false;
 }
 
 __global__ __launch_bounds__(256, 1) void prefix_splitkv_kernel(PrefixArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t lds0[kTileBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t lds1[kTileBytes];
   __shared__ Xchg x;
-  // [tile & 1][key]: slot indices of an upcoming tile.  Its own LDS object, so
-  // the compiler can tell the DMA into it from the exchange area's traffic.
-  __shared__ uint32_t slot_ring[2][64];
 
   Lane ln;
   ln.lane = threadIdx.x & 63;
@@ -217,13 +296,16 @@ __global__ __launch_bounds__(256, 1) void prefix_splitkv_kernel(PrefixArgs a) {
   const int row = tile * kRowTile + row_in_tile;
   const bool row_ok = row < rows_b;
 
-  // the pair's query rows: lane (l32, hl) holds pieces 2s+hl of row l32
-  bf16x8 qf[36];
+  // this wave's half of the pair's query rows: lane (l32, hl) holds, for step
+  // s < 16, latent piece 32*hf + 2s + hl, and for s = 16, 17 rope piece
+  // 4*hf + 2(s-16) + hl (rope pieces start at piece 64)
+  bf16x8 qf[18];
   {
     const uint16_t* qrow = a.q + ((size_t)t0 * a.num_heads + (row_ok ? row : 0)) * kDqk;
 #pragma unroll
-    for (int s2 = 0; s2 < 36; ++s2) {
-      bf16x8 v = *(const bf16x8*)(qrow + (2 * s2 + ln.hl) * 8);
+    for (int s2 = 0; s2 < 18; ++s2) {
+      const int piece = s2 < 16 ? 32 * ln.hf + 2 * s2 + ln.hl : 64 + 4 * ln.hf + 2 * (s2 - 16) + ln.hl;
+      bf16x8 v = *(const bf16x8*)(qrow + piece * 8);
       qf[s2] = row_ok ? v : bf16x8{};
     }
   }
@@ -233,56 +315,83 @@ __global__ __launch_bounds__(256, 1) void prefix_splitkv_kernel(PrefixArgs a) {
   for (int d = 0; d < 8; ++d) o[d] = f32x16{};
   RowState st{-INFINITY, 0.f};
 
-  // lane constants for LDS reads
-  ln.qk_off = ln.hf * 512 + ln.hl * 1024 + ((ln.l32 ^ (8 * ln.hl)) * 16);
+  // lane constants for LDS reads (layout in the header comment)
   {
-    const int g = ln.lane >> 4, sl = ln.lane & 15;
-    const int cpart = 2 * (g & 1) + ((sl >> 1) & 1);
-    const int xr = 8 * ((sl >> 1) & 1);
-    const int keyoff = 4 * ln.hl + (sl >> 2);
-    ln.trb1 = cpart * 1024 + 8 * (sl & 1) + (keyoff + xr) * 16;
-    ln.trb2 = cpart * 1024 + 8 * (sl & 1) + (keyoff + (8 - xr)) * 16;
+    const int key = ln.l32;                                  // + 32*kb, which keeps g and h
+    ln.qk_lat = (key * 1024 + 512 * ln.hf) | ((ln.hl ^ swz_latent(key)) << 4);
+    ln.qk_rope = (kRopeBase + key * 128) | (((4 * ln.hf) ^ ln.hl ^ swz_rope(key)) << 4);
+    // PV: lane (block gb, sub-lane sl) reads keys kb*32 + half*16 + 4*hl + (sl >> 2) (+8*sec),
+    // columns 32*D + 16*(gb & 1) + 4*(sl & 3) .. +3 of output block D = 8*hf + j
+    const int gb = ln.lane >> 4, sl = ln.lane & 15;
+    const int kk = 4 * ln.hl + (sl >> 2);
+    const int cp = 2 * (gb & 1) + ((sl >> 1) & 1);
+#pragma unroll
+    for (int sec = 0; sec < 2; ++sec) {
+      const int gk = (kk << 1) | sec;                        // g(key) of key kk + 8*sec
+      ln.pv[sec] = ((kk + 8 * sec) * 1024 + 512 * ln.hf + 8 * (sl & 1)) | ((cp ^ gk) << 4);
+    }
   }
 
-  // gather lane: this wave writes pieces of parity (w & 1), so lane loads key lane ^ 8*(w&1)
-  const int gkey = ln.lane ^ (8 * (ln.w & 1));
-  const int* slots = a.prefix_slot + p0;
+  // The slot list is read-only for the whole kernel: reading it through the
+  // constant address space makes these uniform loads scalar (s_load, counted
+  // by lgkmcnt), so waiting for them never waits for the in-flight gathers.
+  typedef const __attribute__((address_space(4))) int const_int;
+  const_int* slots = (const_int*)(a.prefix_slot + p0);
   const int ntiles = (kend - kbeg + kKeyTile - 1) / kKeyTile;
-  auto row_of = [&](uint32_t slot) -> const uint16_t* { return a.pool + (size_t)slot * kDqk; };
-  // Slot indices travel to LDS by DMA too, two tiles ahead of their use, so no
-  // register waits on them while gathers are in flight.  Keys past the end of
-  // the chunk read the last key's slot (a valid index; masked in the math).
-  auto slot_dma = [&](int t) {
-    const int key = min(kbeg + t * kKeyTile + ln.lane, kend - 1);
-    __builtin_amdgcn_global_load_lds((const void*)(slots + key), (lds_void*)&slot_ring[t & 1][0], 4, 0, 0);
+  // slots of this wave's 16 keys of tile t (scalars); keys past the end of
+  // the chunk take the last key's slot (a valid index; masked in the math)
+  auto load_slots = [&](int t, uint32_t (&sl)[16]) {
+    const int base = kbeg + t * kKeyTile + 16 * ln.w;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sl[i] = (uint32_t)slots[min(base + i, kend - 1)];
   };
 
-  gather_tile(row_of((uint32_t)slots[min(kbeg + gkey, kend - 1)]), lds0, ln.w);
-  if (ln.w == 0) slot_dma(1);
-
-  for (int t = 0; t < ntiles; t += 2) {
+  uint32_t sl_next[16];
+  // put tile 0 into `buf` (chunk start and restarts)
+  auto prime = [&](uint8_t* buf) {
+    uint32_t sl0[16];
+    load_slots(0, sl0);
+    gather_tile(a.pool, sl0, buf, ln.w, ln.lane);
+    load_slots(1, sl_next);
+  };
+  prime(lds0);
+  int t = 0;                 // tile held by the buffer processed next
+  bool restart = false;      // workgroup-uniform
+  // one tile: `cur` holds tile t while `nxt` receives tile t+1
+  auto half_step = [&](uint8_t* cur, uint8_t* nxt) -> bool {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+    if (restart) {
+      restart = false;
+      t = 0;
+#pragma unroll
+      for (int d = 0; d < 8; ++d) o[d] = f32x16{};
+      st.l = 0.f;
+      prime(cur);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+    } else if (t >= ntiles) {
+      return false;
+    }
     if (t + 1 < ntiles) {
-      gather_tile(row_of(slot_ring[1][gkey]), lds1, ln.w);
-      if (ln.w == 0) slot_dma(t + 2);
+      gather_tile(a.pool, sl_next, nxt, ln.w, ln.lane);
+      load_slots(t + 2, sl_next);
     }
-    tile_math(lds0, x, qf, o, st, min(kKeyTile, kend - kbeg - t * kKeyTile), a.scale_log2, ln);
-    if (t + 1 >= ntiles) break;
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (t + 2 < ntiles) {
-      gather_tile(row_of(slot_ring[0][gkey]), lds0, ln.w);
-      if (ln.w == 0) slot_dma(t + 3);
-    }
-    tile_math(lds1, x, qf, o, st, min(kKeyTile, kend - kbeg - (t + 1) * kKeyTile), a.scale_log2, ln);
+    restart = tile_math(cur, x, qf, o, st, min(kKeyTile, kend - kbeg - t * kKeyTile), a.scale_log2, ln);
+    ++t;
+    return true;
+  };
+  for (;;) {
+    if (!half_step(lds0, lds1)) break;
+    if (!half_step(lds1, lds0)) break;
   }
 
   // row sum: own lane, lane ^ 32, and the partner's two lanes
   const float lpair = st.l + __shfl_xor(st.l, 32);
-  x.lsum[ln.w][ln.lane] = lpair;
+  lds_barrier();                      // everyone is done reading the last P exchange
+  x.v[ln.w][0][ln.lane] = make_float4(lpair, 0.f, 0.f, 0.f);
   lds_barrier();
-  const float l_tot = lpair + x.lsum[ln.w ^ 1][ln.lane];
+  const float l_tot = lpair + x.v[ln.w ^ 1][0][ln.lane].x;
   if (!row_ok) return;
   const float inv = 1.0f / l_tot;
   const size_t pidx = ((size_t)b * a.row_tiles + tile) * a.max_chunks + s;
