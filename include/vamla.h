@@ -87,7 +87,7 @@ typedef struct vamla_params {
   int32_t d_qk;             /* must be 576 */
   int32_t d_v;              /* must be 512 */
   int64_t pool_slots;       /* P >= 1: rows in kv_pool */
-  float softmax_scale;      /* sigma, applied to q.k before the exponential */
+  float softmax_scale;      /* sigma > 0 (finite), applied to q.k before the exponential */
   int32_t max_tree;         /* >= every N_b, in [1, 65] (planning bound) */
   int32_t total_tree;       /* T = cu_tree[B] >= 1 */
   int64_t max_prefix;       /* >= every L_b (planning bound), >= 0 */

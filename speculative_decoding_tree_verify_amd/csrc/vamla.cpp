@@ -35,7 +35,7 @@ int check_shape(const vamla_params* p) {
   if (p->batch < 1 || p->pool_slots < 1 || p->max_prefix < 0 || p->total_prefix < 0 || p->total_tree < 1)
     return VAMLA_ERR_INVALID_ARG;
   if (p->flags != 0) return VAMLA_ERR_INVALID_ARG;
-  if (!(std::isfinite(p->softmax_scale))) return VAMLA_ERR_INVALID_ARG;
+  if (!(std::isfinite(p->softmax_scale) && p->softmax_scale > 0.f)) return VAMLA_ERR_INVALID_ARG;
   if (p->d_qk != VAMLA_D_QK || p->d_v != VAMLA_D_V) return VAMLA_ERR_UNSUPPORTED;
   if (p->num_heads < 1 || p->num_heads > VAMLA_MAX_HEADS) return VAMLA_ERR_UNSUPPORTED;
   if (p->max_tree < 1 || p->max_tree > VAMLA_MAX_TREE) return VAMLA_ERR_UNSUPPORTED;

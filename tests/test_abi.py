@@ -104,6 +104,15 @@ def test_plan_rejects_bad_shapes(L, field, value, code):
     assert e.value.status == code
 
 
+@pytest.mark.parametrize("scale", [0.0, -0.5, float("inf"), float("nan")])
+def test_plan_rejects_bad_scale(L, scale):
+    p = prob(1)
+    p.softmax_scale = scale
+    with pytest.raises(vb.VamlaError) as e:
+        vb.plan(p)
+    assert e.value.status == -1
+
+
 def test_plan_rejects_bad_dims(L):
     p = prob(1).params()
     p.d_qk = 512
