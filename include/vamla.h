@@ -59,7 +59,7 @@ extern "C" {
 #define VAMLA_MAX_TREE 65       /* root + up to 64 drafted nodes */
 #define VAMLA_MAX_HEADS 128
 #define VAMLA_KEY_TILE 64       /* chunk sizes are multiples of this */
-#define VAMLA_ROW_TILE 128      /* query rows per prefix work item */
+#define VAMLA_ROW_TILE 64       /* query rows per prefix work item */
 
 typedef enum vamla_status {
   VAMLA_OK = 0,
@@ -103,14 +103,14 @@ typedef struct vamla_params {
 /* Work decomposition the library derives from vamla_params (host only). */
 typedef struct vamla_plan_info {
   int32_t chunk;            /* prefix keys per split (multiple of 64) */
-  int32_t row_tiles;        /* ceil(max_tree * H / 128): row tiles per request */
+  int32_t row_tiles;        /* ceil(max_tree * H / 64): row tiles per request */
   int32_t max_chunks;       /* ceil(max_prefix / chunk), >= 1 */
   int32_t grid_items;       /* prefix kernel grid (B * row_tiles * max_chunks, padded to 8) */
   /* workspace layout (byte offsets from vamla_params.workspace) */
-  size_t off_part_o;        /* float [B][row_tiles][max_chunks][128 d4][128 rows][4] */
-  size_t off_part_lse;      /* float [B][row_tiles][max_chunks][128 rows] */
-  size_t off_tail_o;        /* float [B][row_tiles][128 d4][128 rows][4] */
-  size_t off_tail_lse;      /* float [B][row_tiles][128 rows] */
+  size_t off_part_o;        /* float [B][row_tiles][max_chunks][128 d4][64 rows][4] */
+  size_t off_part_lse;      /* float [B][row_tiles][max_chunks][64 rows] */
+  size_t off_tail_o;        /* float [B][row_tiles][128 d4][64 rows][4] */
+  size_t off_tail_lse;      /* float [B][row_tiles][64 rows] */
   size_t workspace_bytes;   /* total */
 } vamla_plan_info;
 

@@ -19,6 +19,11 @@ namespace {
 
 using namespace vamla;
 
+static_assert(VAMLA_ROW_TILE == kRowTile, "header row tile must match the kernels");
+static_assert(VAMLA_KEY_TILE == kKeyTile, "header key tile must match the kernels");
+static_assert(VAMLA_D_QK == kDqk && VAMLA_D_V == kDv, "header dims must match the kernels");
+static_assert(VAMLA_MAX_TREE == kMaxTree && VAMLA_MAX_HEADS == kMaxHeads, "header bounds must match the kernels");
+
 // Chunk choice assumes the full MI355X: 256 CUs, one prefix work item per CU
 // at a time (the item's key tiles fill the LDS).
 constexpr int64_t kCUs = 256;
