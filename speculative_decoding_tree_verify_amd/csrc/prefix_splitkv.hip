@@ -31,16 +31,17 @@
 //
 // Gather: global_load_lds_dwordx4 moves 16 bytes per lane straight into LDS
 // (no VGPR staging).  Per key, one instruction fetches the 1 KB latent part of
-// its pool row (8 cache lines) and one 8-lane instruction the 128-byte rope
-// part; the slot of each key is a scalar, loaded one tile ahead.  LDS tile
+// its pool row (8 cache lines); one instruction fetches the 128-byte rope parts
+// of 8 keys.  Slots are held one per lane and loaded two tiles ahead.  LDS tile
 // layout (72 KB per 64 keys):
 //   latent: key k at k*1024, 16-byte piece c at slot c ^ g(k),
-//           g(k) = ((k & 7) << 1) | ((k >> 3) & 1)
+//           g(k) = ((k & 3) << 2) | ((k >> 2) & 3)
 //   rope:   key k at 64 KB + k*128, piece c at slot c ^ ((k >> 1) & 7)
 // Lane-linear DMA writes pick the piece each lane loads, so the swizzle is
-// free; it keeps the ds_read_b128 (QK) and ds_read_b64_tr_b16 (PV) patterns
-// free of bank conflicts.  Tiles are double-buffered: the gather of tile t+1
-// runs under the math of tile t.
+// free; it keeps the ds_read_b128 (QK, 16 lanes per LDS cycle) and
+// ds_read_b64_tr_b16 (PV, 32 lanes per cycle) patterns free of bank
+// conflicts.  Tiles are double-buffered: the 18 gather instructions of tile
+// t+1 are spread over the QK loop of tile t.
 //
 // Softmax reference: each row keeps a reference m (log2 units) instead of a
 // running max, so the accumulator is never rescaled and stays in AGPRs.  The
@@ -74,7 +75,7 @@ struct __attribute__((aligned(16))) Xchg {
   float4 v[4][4][64];               // [wave][16-byte part][lane], 16 KB
 };
 
-__device__ __forceinline__ int swz_latent(int k) { return ((k & 7) << 1) | ((k >> 3) & 1); }
+__device__ __forceinline__ int swz_latent(int k) { return ((k & 3) << 2) | ((k >> 2) & 3); }
 __device__ __forceinline__ int swz_rope(int k) { return (k >> 1) & 7; }
 
 // Workgroup barrier that waits only for this wave's LDS operations.  A fence
@@ -100,28 +101,38 @@ __device__ __forceinline__ bf16x8 tr_pair(const uint8_t* base, int off1, int off
   return __builtin_bit_cast(bf16x8, v);
 }
 
-// Part `part` (keys [16w + 4*part, 16w + 4*part + 4)) of this wave's share of
-// one key tile; `sl` holds the slots of the wave's 16 keys.
-__device__ __forceinline__ void gather_part(const uint16_t* pool, const uint32_t (&sl)[16], uint8_t* lds, int w,
-                                            int lane, int part) {
-  const int lane16 = lane << 4;
-#pragma unroll
-  for (int i = 4 * part; i < 4 * part + 4; ++i) {
-    const uint8_t* row = (const uint8_t*)(pool + (size_t)sl[i] * kDqk);
-    const int k = 16 * w + i;
-    __builtin_amdgcn_global_load_lds((const void*)(row + (uint32_t)xor_at_use(lane16, swz_latent(i) << 4)),
-                                     (lds_void*)(lds + k * 1024), 16, 0, 0);
-    if (lane < 8)
-      __builtin_amdgcn_global_load_lds(
-          (const void*)(row + 1024 + (uint32_t)xor_at_use(lane16, swz_rope(i) << 4)),
-          (lds_void*)(lds + kRopeBase + k * 128), 16, 0, 0);
+// Pool slots of one wave's 16 keys of a tile, one per lane: `lat` holds the
+// slot of key 16w + (lane & 15), rope[j] that of key 16w + 8j + (lane >> 3).
+struct TileSlots {
+  uint32_t lat, rope[2];
+};
+
+// Gather instruction d (0..17) of this wave's share of one key tile, keys
+// [16w, 16w+16): d < 16 moves the 1 KB latent part of key 16w+d (one 64-lane
+// instruction, 8 cache lines; the slot is read out of lane d), d = 16, 17 the
+// 128-byte rope parts of keys 16w + 8(d-16) + (lane >> 3) (8 keys per 64-lane
+// instruction).  Lanes write 16 bytes each, lane-linearly, and load the piece
+// the swizzle puts there.
+__device__ __forceinline__ void gather_one(const uint16_t* pool, const TileSlots& sl, uint8_t* lds, int w, int lane,
+                                           int d) {
+  if (d < 16) {
+    const uint32_t slot = __builtin_amdgcn_readlane(sl.lat, d);
+    const uint8_t* row = (const uint8_t*)(pool + (size_t)slot * kDqk);
+    __builtin_amdgcn_global_load_lds((const void*)(row + (uint32_t)xor_at_use(lane << 4, swz_latent(d) << 4)),
+                                     (lds_void*)(lds + (16 * w + d) * 1024), 16, 0, 0);
+  } else {
+    const int j = d - 16;
+    const int kl = 8 * j + (lane >> 3);                      // key within the wave's 16
+    const uint8_t* row = (const uint8_t*)(pool + (size_t)sl.rope[j] * kDqk + 512);
+    __builtin_amdgcn_global_load_lds((const void*)(row + (uint32_t)(((lane & 7) ^ swz_rope(kl)) << 4)),
+                                     (lds_void*)(lds + kRopeBase + (16 * w + 8 * j) * 128), 16, 0, 0);
   }
 }
 
-__device__ __forceinline__ void gather_tile(const uint16_t* pool, const uint32_t (&sl)[16], uint8_t* lds, int w,
+__device__ __forceinline__ void gather_tile(const uint16_t* pool, const TileSlots& sl, uint8_t* lds, int w,
                                             int lane) {
 #pragma unroll
-  for (int part = 0; part < 4; ++part) gather_part(pool, sl, lds, w, lane, part);
+  for (int d = 0; d < 18; ++d) gather_one(pool, sl, lds, w, lane, d);
 }
 
 struct Lane {
@@ -161,7 +172,8 @@ __device__ __forceinline__ void pack_p(const f32x16& v, float scale, float m, bf
 // must restart its chunk (this tile was not accumulated).
 __device__ __forceinline__ bool tile_math(const uint8_t* lds, Xchg& x, const bf16x8 (&qf)[18],
                                           f32x16 (&o)[8], RowState& st, int nvalid, float scale_log2,
-                                          const Lane& ln) {
+                                          const Lane& ln, const uint16_t* pool, const TileSlots& ng_sl,
+                                          uint8_t* ng_lds) {
   // partial S^T over this wave's d-half, key blocks 0 and 1 interleaved so
   // consecutive MFMAs never depend on each other
   f32x16 sp0 = {}, sp1 = {};
@@ -176,6 +188,10 @@ __device__ __forceinline__ bool tile_math(const uint8_t* lds, Xchg& x, const bf1
       if (i + kPre < 36) kf[i % kPre] = kfrag(lds, ln, (i + kPre) & 1, (i + kPre) >> 1);
       if (kb) sp1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur, qf[s], sp1, 0, 0, 0);
       else sp0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur, qf[s], sp0, 0, 0, 0);
+      // the gather of the next tile rides along, one instruction per two MFMAs:
+      // issuing it all at once stalls the wave on the full address queue.  On
+      // a chunk's last tile it refetches valid rows into the idle buffer.
+      if ((i & 1) == 0) gather_one(pool, ng_sl, ng_lds, ln.w, ln.lane, i >> 1);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
@@ -327,32 +343,30 @@ __global__ __launch_bounds__(256, 1) void prefix_splitkv_kernel(PrefixArgs a) {
     const int cp = 2 * (gb & 1) + ((sl >> 1) & 1);
 #pragma unroll
     for (int sec = 0; sec < 2; ++sec) {
-      const int gk = (kk << 1) | sec;                        // g(key) of key kk + 8*sec
+      const int gk = ((sl >> 2) << 2) | (ln.hl + 2 * sec);   // g(key) of key kk + 8*sec
       ln.pv[sec] = ((kk + 8 * sec) * 1024 + 512 * ln.hf + 8 * (sl & 1)) | ((cp ^ gk) << 4);
     }
   }
 
-  // The slot list is read-only for the whole kernel: reading it through the
-  // constant address space makes these uniform loads scalar (s_load, counted
-  // by lgkmcnt), so waiting for them never waits for the in-flight gathers.
-  typedef const __attribute__((address_space(4))) int const_int;
-  const_int* slots = (const_int*)(a.prefix_slot + p0);
+  // Slots of this wave's keys of tile t, one vector load per lane (see
+  // TileSlots); keys past the end of the chunk take the last key's slot (a
+  // valid index; masked in the math).
+  const int* slots = a.prefix_slot + p0;
   const int ntiles = (kend - kbeg + kKeyTile - 1) / kKeyTile;
-  // slots of this wave's 16 keys of tile t (scalars); keys past the end of
-  // the chunk take the last key's slot (a valid index; masked in the math)
-  auto load_slots = [&](int t, uint32_t (&sl)[16]) {
+  auto load_slots = [&](int t) {
     const int base = kbeg + t * kKeyTile + 16 * ln.w;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) sl[i] = (uint32_t)slots[min(base + i, kend - 1)];
+    TileSlots r;
+    r.lat = (uint32_t)slots[min(base + (ln.lane & 15), kend - 1)];
+    r.rope[0] = (uint32_t)slots[min(base + (ln.lane >> 3), kend - 1)];
+    r.rope[1] = (uint32_t)slots[min(base + 8 + (ln.lane >> 3), kend - 1)];
+    return r;
   };
 
-  uint32_t sl_next[16];
+  TileSlots sl_next;
   // put tile 0 into `buf` (chunk start and restarts)
   auto prime = [&](uint8_t* buf) {
-    uint32_t sl0[16];
-    load_slots(0, sl0);
-    gather_tile(a.pool, sl0, buf, ln.w, ln.lane);
-    load_slots(1, sl_next);
+    gather_tile(a.pool, load_slots(0), buf, ln.w, ln.lane);
+    sl_next = load_slots(1);
   };
   prime(lds0);
   int t = 0;                 // tile held by the buffer processed next
@@ -373,11 +387,10 @@ __global__ __launch_bounds__(256, 1) void prefix_splitkv_kernel(PrefixArgs a) {
     } else if (t >= ntiles) {
       return false;
     }
-    if (t + 1 < ntiles) {
-      gather_tile(a.pool, sl_next, nxt, ln.w, ln.lane);
-      load_slots(t + 2, sl_next);
-    }
-    restart = tile_math(cur, x, qf, o, st, min(kKeyTile, kend - kbeg - t * kKeyTile), a.scale_log2, ln);
+    restart = tile_math(cur, x, qf, o, st, min(kKeyTile, kend - kbeg - t * kKeyTile), a.scale_log2, ln, a.pool,
+                        sl_next, nxt);
+    // slots of tile t+2; their latency hides under the wait for tile t+1
+    sl_next = load_slots(t + 2);
     ++t;
     return true;
   };
