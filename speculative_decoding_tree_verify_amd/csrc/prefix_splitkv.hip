@@ -29,8 +29,12 @@
 // Per wave: Q 72 VGPRs, a 32x256 fp32 accumulator (128), so the compiler has
 // room to keep the LDS operand reads several MFMAs ahead.
 //
-// Gather: global_load_lds_dwordx4 moves 16 bytes per lane straight into LDS
-// (no VGPR staging).  Per key, one instruction fetches the 1 KB latent part of
+// Gather: buffer_load_dwordx4 ... lds moves 16 bytes per lane straight into
+// LDS (no VGPR staging).  Latent rows use the buffer (MUBUF) form with one
+// descriptor per row, rope rows the global form issued through asm (see
+// dma16_global): the compiler counts a global LDS-DMA as a pending LDS access
+// until it completes, which would turn every LDS operand wait of the tile
+// into a full drain; a buffer DMA is tracked as a plain vector-memory op.  Per key, one instruction fetches the 1 KB latent part of
 // its pool row (8 cache lines); one instruction fetches the 128-byte rope parts
 // of 8 keys.  Slots are held one per lane and loaded two tiles ahead.  LDS tile
 // layout (72 KB per 64 keys):
@@ -67,6 +71,8 @@ constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kSlack = 16.0f;     // scores may exceed the reference by this much (log2 units)
 constexpr int kRopeBase = 64 * 1024;
 constexpr int kPre = 4;             // LDS operand reads in flight ahead of their MFMA
+// Buffer descriptor word 3 for plain dword loads (32-bit data format, no swizzle)
+constexpr int kRsrcWord3 = 0x00020000;
 
 // Exchange area: per wave, 64 bytes per lane.  Wave w writes its partial
 // scores for the partner's key block into v[w]; the partner reads them and
@@ -101,6 +107,26 @@ __device__ __forceinline__ bf16x8 tr_pair(const uint8_t* base, int off1, int off
   return __builtin_bit_cast(bf16x8, v);
 }
 
+// LDS DMA of 16 bytes per lane from a 64-bit per-lane address into LDS at
+// lds_addr + 16*lane (the rope parts of 8 keys from 8 unrelated rows; buffer
+// offsets are 32-bit, so rows past 4 GiB of the pool need this form).  Written
+// as asm so that the compiler's wait tracking does not see it: it would count
+// the op as a pending LDS access until it completes and drain every LDS wait
+// behind it.  The data is read only after the s_waitcnt 0 and barrier that
+// start the next tile.  M0 carries the LDS address and is restored.
+__device__ __forceinline__ void dma16_global(const void* src, uint32_t lds_addr) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(src), "s"(lds_addr)
+      : "memory");
+}
+
 // Pool slots of one wave's 16 keys of a tile, one per lane: `lat` holds the
 // slot of key 16w + (lane & 15), rope[j] that of key 16w + 8j + (lane >> 3).
 struct TileSlots {
@@ -117,15 +143,15 @@ __device__ __forceinline__ void gather_one(const uint16_t* pool, const TileSlots
                                            int d) {
   if (d < 16) {
     const uint32_t slot = __builtin_amdgcn_readlane(sl.lat, d);
-    const uint8_t* row = (const uint8_t*)(pool + (size_t)slot * kDqk);
-    __builtin_amdgcn_global_load_lds((const void*)(row + (uint32_t)xor_at_use(lane << 4, swz_latent(d) << 4)),
-                                     (lds_void*)(lds + (16 * w + d) * 1024), 16, 0, 0);
+    const __amdgpu_buffer_rsrc_t row = __builtin_amdgcn_make_buffer_rsrc((void*)(pool + (size_t)slot * kDqk), 0, 1024,
+                                                                         kRsrcWord3);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(row, (lds_void*)(lds + (16 * w + d) * 1024), 16,
+                                             (uint32_t)xor_at_use(lane << 4, swz_latent(d) << 4), 0, 0, 0);
   } else {
     const int j = d - 16;
     const int kl = 8 * j + (lane >> 3);                      // key within the wave's 16
-    const uint8_t* row = (const uint8_t*)(pool + (size_t)sl.rope[j] * kDqk + 512);
-    __builtin_amdgcn_global_load_lds((const void*)(row + (uint32_t)(((lane & 7) ^ swz_rope(kl)) << 4)),
-                                     (lds_void*)(lds + kRopeBase + (16 * w + 8 * j) * 128), 16, 0, 0);
+    const uint8_t* src = (const uint8_t*)(pool + (size_t)sl.rope[j] * kDqk + 512) + (((lane & 7) ^ swz_rope(kl)) << 4);
+    dma16_global(src, (uint32_t)(uintptr_t)(lds_void*)(lds + kRopeBase + (16 * w + 8 * j) * 128));
   }
 }
 

@@ -223,3 +223,35 @@ def test_defragmented_pool_gives_identical_result():
               tree_slot_idx=torch.arange(n + 1, n + 1 + x.total_tree, dtype=torch.int32, device="cuda"))
     o2, l2, _ = run_verify(x, dev=d2)
     assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+def test_rows_beyond_4gib_of_pool():
+    # Every row the step reads sits past byte 2^32 of a 4.6 GB pool whose other
+    # rows are NaN: addressing that lost the high bits of slot * 1152 would
+    # land inside the pool on a NaN row.
+    import torch
+    rng = np.random.default_rng(10)
+    x = small([700, 130], [gen.random_tree(9, rng), gen.chain_plus_branch()], 8, seed=22)
+    big = 4_000_000
+    base = (1 << 32) // 1152 + 1000
+    used = np.concatenate([x.prefix_slot_idx, x.tree_slot_idx]).astype(np.int64)
+    uniq = np.unique(used)
+    remap = np.full(x.pool.shape[0], -1, np.int64)
+    remap[uniq] = base + rng.permutation(len(uniq))
+    assert remap[uniq].max() < big
+    d = to_dev(x)
+    pool = torch.full((big, 576), float("nan"), dtype=torch.bfloat16, device="cuda")
+    pool[torch.from_numpy(remap[uniq]).cuda()] = d["kv_pool"][torch.from_numpy(uniq).cuda()]
+    d = dict(d, kv_pool=pool,
+             prefix_slot_idx=torch.from_numpy(remap[x.prefix_slot_idx].astype(np.int32)).cuda(),
+             tree_slot_idx=torch.from_numpy(remap[x.tree_slot_idx].astype(np.int32)).cuda())
+    log(f"[case] pool of {big} slots, rows at slots >= {base}")
+    p = vb.Problem.from_host(x.cu_prefix, x.cu_tree, x.num_heads, big, x.scale, chunk=256)
+    out, lse = vb.verify_attn_mla(p, d["q"], d["kv_pool"], d["prefix_slot_idx"], d["tree_slot_idx"], d["parent"],
+                                  d["cu_prefix"], d["cu_tree"])
+    torch.cuda.synchronize()
+    ro, rl = oracle_full(x)
+    assert_close_lse(lse.cpu().numpy().astype(np.float64), rl, "beyond 4 GiB")
+    assert_close_out(out.float().cpu().numpy().astype(np.float64), ro, "beyond 4 GiB")
+    del pool
+    torch.cuda.empty_cache()
