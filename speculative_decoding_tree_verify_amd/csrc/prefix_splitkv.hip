@@ -14,20 +14,21 @@
 // (v_mfma_f32_32x32x16_bf16, fp32 accumulation).
 //
 // Waves form two pairs; pair p owns query rows [32p, 32p+32) of the tile and
-// wave (p, h) of the pair:
-//   * QK: holds half of the 576 query columns (latent [256h, 256h+256) and
-//     rope [32h, 32h+32)) in VGPRs and computes the partial scores S^T = K Q^T
-//     over that half for all 64 keys of the tile (A = K from LDS, B = Q).  In
-//     the 32x32 accumulator layout each lane owns one query row.
-//   * exchange: keeps the partial of key block h, sends the other block to its
-//     partner through LDS; adding the partner's half gives the full scores of
-//     keys [32h, 32h+32).
-//   * softmax: P = exp2(S*scale*log2e - m) in bf16 for those 32 keys, sent to
-//     the partner lane for lane (it is the partner's MFMA operand as well).
-//   * PV: O^T += V^T P^T for output columns [256h, 256h+256) over all 64 keys
-//     (A = V^T read from the same LDS tile by ds_read_b64_tr_b16, B = P).
-// Per wave: Q 72 VGPRs, a 32x256 fp32 accumulator (128), so the compiler has
-// room to keep the LDS operand reads several MFMAs ahead.
+// wave (p, h) of the pair key block h (keys [32h, 32h+32) of each tile) and
+// output columns [256h, 256h+256):
+//   * QK: holds all 576 query columns of the pair's rows in VGPRs and computes
+//     the scores S^T = K Q^T of its key block (A = K from LDS, B = Q).  In the
+//     32x32 accumulator layout each lane owns one query row.
+//   * softmax: P = exp2(S*scale*log2e - m) in bf16 for those 32 keys, also
+//     stored to LDS for the partner (it is the partner's MFMA operand too).
+//   * PV: O^T += V^T P^T for its 256 output columns over all 64 keys (A = V^T
+//     read from the same LDS tile by ds_read_b64_tr_b16, B = P): first over
+//     its own key block, then, after the tile's one barrier, over the
+//     partner's with the P the partner stored.
+// Per wave: Q 144 VGPRs and a 32x256 fp32 accumulator (128 AGPRs).  Splitting
+// the pair by keys rather than by query columns leaves no partial scores to
+// exchange, so a tile needs one barrier besides the one that hands over the
+// staged tile.
 //
 // Gather: buffer_load_dwordx4 ... lds moves 16 bytes per lane straight into
 // LDS (no VGPR staging).  Latent rows use the buffer (MUBUF) form with one
@@ -70,15 +71,21 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kSlack = 16.0f;     // scores may exceed the reference by this much (log2 units)
 constexpr int kRopeBase = 64 * 1024;
-constexpr int kPre = 4;             // LDS operand reads in flight ahead of their MFMA
+constexpr int kPreQK = 4;           // LDS operand reads in flight ahead of their MFMA (QK)
+constexpr int kPrePV = 4;           // same for PV (two transposed reads each)
+constexpr int kQkSteps = kDqk / 16; // 36 MFMA steps over the query columns
+
+// Which gather instruction of the next tile (0..17, or -1 for none) rides
+// along with QK step i (0..35).  Issuing them spread out keeps the wave from
+// stalling on a full address queue.
+__device__ __forceinline__ constexpr int qk_dma(int i) { return (i & 1) == 0 ? (i >> 1) : -1; }
 // Buffer descriptor word 3 for plain dword loads (32-bit data format, no swizzle)
 constexpr int kRsrcWord3 = 0x00020000;
 
-// Exchange area: per wave, 64 bytes per lane.  Wave w writes its partial
-// scores for the partner's key block into v[w]; the partner reads them and
-// then reuses that same slot to send back its P operands and tile max.
+// Exchange area, 48 bytes per lane and wave: wave w stores the P operand of
+// its key block in v[w][0..1] and its row max and restart vote in v[w][2].
 struct __attribute__((aligned(16))) Xchg {
-  float4 v[4][4][64];               // [wave][16-byte part][lane], 16 KB
+  float4 v[4][3][64];               // [wave][16-byte part][lane], 12 KB
 };
 
 __device__ __forceinline__ int swz_latent(int k) { return ((k & 3) << 2) | ((k >> 2) & 3); }
@@ -164,8 +171,9 @@ __device__ __forceinline__ void gather_tile(const uint16_t* pool, const TileSlot
 struct Lane {
   int w, pr, hf, hl, l32, lane;
   // Swizzled LDS addresses are written base ^ (step-dependent bits) + immediate:
-  int qk_lat;        // latent: key*1024 + 512*hf | ((hl ^ g(key)) << 4); step s: ^ 32*(s&7), + 256*(s>>3)
-  int qk_rope;       // rope: 64K + key*128 | ((4*hf ^ hl ^ h(key)) << 4); rope step r: ^ 32*r
+  // key = 32*hf + l32 (the lane's key of the wave's block)
+  int qk_lat;        // latent: key*1024 | ((hl ^ g(key)) << 4); step s: ^ 32*(s&7), + 256*(s>>3)
+  int qk_rope;       // rope: 64K + key*128 | ((hl ^ h(key)) << 4); rope step r: ^ 32*r
   int pv[2];         // PV transposed reads, key group sec: column block d: ^ 64*(d&3), + 256*(d>>2)
 };
 
@@ -174,11 +182,32 @@ struct RowState {
   float l;   // this lane's share of the row sum
 };
 
-// K fragment of QK step s for key block kb: this wave's d-half, pieces
-// 2s and 2s+1 of it (lane half hl takes 2s+hl).
-__device__ __forceinline__ bf16x8 kfrag(const uint8_t* lds, const Lane& ln, int kb, int s) {
-  if (s < 16) return *(const bf16x8*)(lds + xor_at_use(ln.qk_lat, 32 * (s & 7)) + (s >> 3) * 256 + kb * 32768);
-  return *(const bf16x8*)(lds + xor_at_use(ln.qk_rope, 32 * (s - 16)) + kb * 4096);
+// K fragment of QK step s (0..35) of this wave's key block: 16-byte pieces
+// 2s and 2s+1 of the 576 columns (latent for s < 32, then rope); lane half
+// hl takes piece 2s + hl.
+__device__ __forceinline__ bf16x8 kfrag(const uint8_t* lds, const Lane& ln, int s) {
+  if (s < 32) return *(const bf16x8*)(lds + xor_at_use(ln.qk_lat, 32 * (s & 7)) + (s >> 3) * 256);
+  return *(const bf16x8*)(lds + xor_at_use(ln.qk_rope, 32 * (s - 32)));
+}
+
+// x[lane] and x[lane ^ 32] for every lane, through one v_permlane32_swap of
+// two copies of x (afterwards each lane holds one of the two values in each
+// register).  Written as asm: handed the same value twice, the builtin's two
+// results get folded into one.
+__device__ __forceinline__ void halves32(float x, float& p, float& q) {
+  p = x;
+  q = x;
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(p), "+v"(q));
+}
+__device__ __forceinline__ float max_xor32(float x) {
+  float p, q;
+  halves32(x, p, q);
+  return fmaxf(p, q);
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+  float p, q;
+  halves32(x, p, q);
+  return p + q;
 }
 
 // P = exp2(s*scale - m) in bf16 for this lane's 16 raw scores; lsum += sum P.
@@ -194,48 +223,56 @@ __device__ __forceinline__ void pack_p(const f32x16& v, float scale, float m, bf
   }
 }
 
-// One staged 64-key tile for this wave.  Returns true when the workgroup
-// must restart its chunk (this tile was not accumulated).
-__device__ __forceinline__ bool tile_math(const uint8_t* lds, Xchg& x, const bf16x8 (&qf)[18],
-                                          f32x16 (&o)[8], RowState& st, int nvalid, float scale_log2,
+// O^T += V^T P^T over key block kb (two 16-key MFMA steps) for this wave's
+// 256 output columns; the eight column blocks interleave so consecutive MFMAs
+// are independent.  P keeps the key order of the score accumulator layout,
+// and the transposed V reads take the keys in that same order.
+__device__ __forceinline__ void pv_block(const uint8_t* lds, const Lane& ln, int kb, const bf16x8 (&p)[2],
+                                         f32x16 (&o)[8]) {
+  const int b0 = ln.pv[0] + kb * 32768, b1 = ln.pv[1] + kb * 32768;
+  auto vfrag = [&](int i) {   // i = half*8 + j
+    const int j = i & 7, half = i >> 3;
+    const int off = half * 16 * 1024 + (j >> 2) * 256;
+    return tr_pair(lds, xor_at_use(b0, 64 * (j & 3)) + off, xor_at_use(b1, 64 * (j & 3)) + off);
+  };
+  bf16x8 vf[kPrePV];
+#pragma unroll
+  for (int i = 0; i < kPrePV; ++i) vf[i] = vfrag(i);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const bf16x8 cur = vf[i % kPrePV];
+    if (i + kPrePV < 16) vf[i % kPrePV] = vfrag(i + kPrePV);
+    o[i & 7] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur, p[i >> 3], o[i & 7], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// One staged 64-key tile for this wave.  `first` (workgroup-uniform): the
+// chunk's reference m is not set yet.  Returns true when the workgroup must
+// restart its chunk; the tile's contribution is then discarded.
+__device__ __forceinline__ bool tile_math(const uint8_t* lds, Xchg& x, const bf16x8 (&qf)[kQkSteps],
+                                          f32x16 (&o)[8], RowState& st, bool first, int nvalid, float scale_log2,
                                           const Lane& ln, const uint16_t* pool, const TileSlots& ng_sl,
                                           uint8_t* ng_lds) {
-  // partial S^T over this wave's d-half, key blocks 0 and 1 interleaved so
-  // consecutive MFMAs never depend on each other
+  // S^T of this wave's key block over all 576 columns; even and odd steps
+  // accumulate separately so consecutive MFMAs never depend on each other
   f32x16 sp0 = {}, sp1 = {};
   {
-    bf16x8 kf[kPre];
+    bf16x8 kf[kPreQK];
 #pragma unroll
-    for (int i = 0; i < kPre; ++i) kf[i] = kfrag(lds, ln, i & 1, i >> 1);
+    for (int i = 0; i < kPreQK; ++i) kf[i] = kfrag(lds, ln, i);
 #pragma unroll
-    for (int i = 0; i < 36; ++i) {
-      const int kb = i & 1, s = i >> 1;
-      const bf16x8 cur = kf[i % kPre];
-      if (i + kPre < 36) kf[i % kPre] = kfrag(lds, ln, (i + kPre) & 1, (i + kPre) >> 1);
-      if (kb) sp1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur, qf[s], sp1, 0, 0, 0);
-      else sp0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur, qf[s], sp0, 0, 0, 0);
-      // the gather of the next tile rides along, one instruction per two MFMAs:
-      // issuing it all at once stalls the wave on the full address queue.  On
-      // a chunk's last tile it refetches valid rows into the idle buffer.
-      if ((i & 1) == 0) gather_one(pool, ng_sl, ng_lds, ln.w, ln.lane, i >> 1);
+    for (int i = 0; i < kQkSteps; ++i) {
+      const bf16x8 cur = kf[i % kPreQK];
+      if (i + kPreQK < kQkSteps) kf[i % kPreQK] = kfrag(lds, ln, i + kPreQK);
+      if (i & 1) sp1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur, qf[i], sp1, 0, 0, 0);
+      else sp0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur, qf[i], sp0, 0, 0, 0);
+      // on a chunk's last tile the gather refetches valid rows into the idle buffer
+      if (qk_dma(i) >= 0) gather_one(pool, ng_sl, ng_lds, ln.w, ln.lane, qk_dma(i));
       __builtin_amdgcn_sched_barrier(0);
     }
   }
-  // send the partner its key block, take ours
-  const f32x16 give = ln.hf ? sp0 : sp1;
-  f32x16 v = ln.hf ? sp1 : sp0;
-#pragma unroll
-  for (int q = 0; q < 4; ++q)
-    x.v[ln.w][q][ln.lane] = make_float4(give[4 * q], give[4 * q + 1], give[4 * q + 2], give[4 * q + 3]);
-  lds_barrier();
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const float4 t = x.v[ln.w ^ 1][q][ln.lane];
-    v[4 * q] += t.x;
-    v[4 * q + 1] += t.y;
-    v[4 * q + 2] += t.z;
-    v[4 * q + 3] += t.w;
-  }
+  f32x16 v = sp0 + sp1;
   // lane holds keys 32*hf + 8*(r/4) + 4*hl + r%4 of row l32 (raw scores)
   if (nvalid < kKeyTile) {
 #pragma unroll
@@ -245,60 +282,37 @@ __device__ __forceinline__ bool tile_math(const uint8_t* lds, Xchg& x, const bf1
   float mt = v[0];
 #pragma unroll
   for (int r = 1; r < 16; ++r) mt = fmaxf(mt, v[r]);
-  mt = fmaxf(mt, __shfl_xor(mt, 32)) * scale_log2;          // row max over my 32 keys, log2 units
-  // P against the current reference, sent in the slot just read
-  float lsum = 0.f;
+  mt = max_xor32(mt) * scale_log2;                 // row max over the block's 32 keys, log2 units
+  if (first) {
+    // the reference is the pair's max over this tile
+    x.v[ln.w][2][ln.lane] = make_float4(mt, 0.f, 0.f, 0.f);
+    lds_barrier();
+    st.m = fmaxf(mt, x.v[ln.w ^ 1][2][ln.lane].x);
+  }
   bf16x8 pb[2];
+  float lsum = 0.f;
   pack_p(v, scale_log2, st.m, pb, lsum);
-  const float want = __any(mt > st.m + kSlack) ? 1.f : 0.f;
-  x.v[ln.w ^ 1][0][ln.lane] = __builtin_bit_cast(float4, pb[0]);
-  x.v[ln.w ^ 1][1][ln.lane] = __builtin_bit_cast(float4, pb[1]);
-  x.v[ln.w ^ 1][2][ln.lane] = make_float4(mt, want, 0.f, 0.f);
+  const float want = __any(mt > st.m + kSlack) ? 1.f : 0.f;   // never on the first tile
+  x.v[ln.w][0][ln.lane] = __builtin_bit_cast(float4, pb[0]);
+  x.v[ln.w][1][ln.lane] = __builtin_bit_cast(float4, pb[1]);
+  x.v[ln.w][2][ln.lane] = make_float4(mt, want, 0.f, 0.f);
+  pv_block(lds, ln, ln.hf, pb, o);                  // discarded if the chunk restarts
   lds_barrier();
-  // every wave stored its wave-uniform flag in all lanes, so read at own lane
+  // every wave stored its wave-uniform vote in all lanes, so read at own lane
   const float any_flag = x.v[0][2][ln.lane].y + x.v[1][2][ln.lane].y + x.v[2][2][ln.lane].y + x.v[3][2][ln.lane].y;
   if (__builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, any_flag)) != 0) {
-    // pair max of this tile (both waves of the pair compute the same value)
-    const float mp = fmaxf(mt, x.v[ln.w][2][ln.lane].x);
-    if (__builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, st.m)) != __builtin_bit_cast(int, -INFINITY)) {
-      // a score ran past the reference: restart the chunk with headroom
-      st.m = fmaxf(st.m, mp) + kSlack;
-      return true;
-    }
-    // first tile of the chunk: take the pair max as the reference; the
-    // accumulators are still zero, so only P is recomputed
-    st.m = mp;
-    lsum = 0.f;
-    pack_p(v, scale_log2, st.m, pb, lsum);
-    lds_barrier();
-    x.v[ln.w ^ 1][0][ln.lane] = __builtin_bit_cast(float4, pb[0]);
-    x.v[ln.w ^ 1][1][ln.lane] = __builtin_bit_cast(float4, pb[1]);
-    lds_barrier();
+    // a score ran past the reference: restart the chunk with headroom
+    const float mp = fmaxf(mt, x.v[ln.w ^ 1][2][ln.lane].x);
+    st.m = fmaxf(st.m, mp) + kSlack;
+    st.l = 0.f;
+#pragma unroll
+    for (int d = 0; d < 8; ++d) o[d] = f32x16{};
+    return true;
   }
   st.l += lsum;
-  const bf16x8 pq0 = __builtin_bit_cast(bf16x8, x.v[ln.w][0][ln.lane]);
-  const bf16x8 pq1 = __builtin_bit_cast(bf16x8, x.v[ln.w][1][ln.lane]);
-  // O^T += V^T P^T for this wave's 256 output columns over all 64 keys;
-  // the eight column blocks are interleaved so consecutive MFMAs are independent
-  {
-    auto vfrag = [&](int i) {   // i = (kb*2 + half)*8 + j
-      const int j = i & 7, kb = i >> 4, half = (i >> 3) & 1;
-      const int off = (kb * 32 + half * 16) * 1024 + (j >> 2) * 256;
-      return tr_pair(lds, xor_at_use(ln.pv[0], 64 * (j & 3)) + off, xor_at_use(ln.pv[1], 64 * (j & 3)) + off);
-    };
-    bf16x8 vf[kPre];
-#pragma unroll
-    for (int i = 0; i < kPre; ++i) vf[i] = vfrag(i);
-#pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      const int j = i & 7, kb = i >> 4, half = (i >> 3) & 1;
-      const bf16x8 cur = vf[i % kPre];
-      if (i + kPre < 32) vf[i % kPre] = vfrag(i + kPre);
-      const bf16x8 bop = (kb == ln.hf) ? pb[half] : (half ? pq1 : pq0);
-      o[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur, bop, o[j], 0, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  }
+  const bf16x8 pq[2] = {__builtin_bit_cast(bf16x8, x.v[ln.w ^ 1][0][ln.lane]),
+                        __builtin_bit_cast(bf16x8, x.v[ln.w ^ 1][1][ln.lane])};
+  pv_block(lds, ln, ln.hf ^ 1, pq, o);
   return false;
 }
 
@@ -338,15 +352,14 @@ __global__ __launch_bounds__(256, 1) void prefix_splitkv_kernel(PrefixArgs a) {
   const int row = tile * kRowTile + row_in_tile;
   const bool row_ok = row < rows_b;
 
-  // this wave's half of the pair's query rows: lane (l32, hl) holds, for step
-  // s < 16, latent piece 32*hf + 2s + hl, and for s = 16, 17 rope piece
-  // 4*hf + 2(s-16) + hl (rope pieces start at piece 64)
-  bf16x8 qf[18];
+  // the pair's query rows, all 576 columns: lane (l32, hl) holds 16-byte
+  // piece 2s + hl of its row for step s (latent pieces 0..63, rope 64..71)
+  bf16x8 qf[kQkSteps];
   {
     const uint16_t* qrow = a.q + ((size_t)t0 * a.num_heads + (row_ok ? row : 0)) * kDqk;
 #pragma unroll
-    for (int s2 = 0; s2 < 18; ++s2) {
-      const int piece = s2 < 16 ? 32 * ln.hf + 2 * s2 + ln.hl : 64 + 4 * ln.hf + 2 * (s2 - 16) + ln.hl;
+    for (int s2 = 0; s2 < kQkSteps; ++s2) {
+      const int piece = 2 * s2 + ln.hl;
       bf16x8 v = *(const bf16x8*)(qrow + piece * 8);
       qf[s2] = row_ok ? v : bf16x8{};
     }
@@ -359,9 +372,9 @@ __global__ __launch_bounds__(256, 1) void prefix_splitkv_kernel(PrefixArgs a) {
 
   // lane constants for LDS reads (layout in the header comment)
   {
-    const int key = ln.l32;                                  // + 32*kb, which keeps g and h
-    ln.qk_lat = (key * 1024 + 512 * ln.hf) | ((ln.hl ^ swz_latent(key)) << 4);
-    ln.qk_rope = (kRopeBase + key * 128) | (((4 * ln.hf) ^ ln.hl ^ swz_rope(key)) << 4);
+    const int key = 32 * ln.hf + ln.l32;
+    ln.qk_lat = (key * 1024) | ((ln.hl ^ swz_latent(key)) << 4);
+    ln.qk_rope = (kRopeBase + key * 128) | ((ln.hl ^ swz_rope(key)) << 4);
     // PV: lane (block gb, sub-lane sl) reads keys kb*32 + half*16 + 4*hl + (sl >> 2) (+8*sec),
     // columns 32*D + 16*(gb & 1) + 4*(sl & 3) .. +3 of output block D = 8*hf + j
     const int gb = ln.lane >> 4, sl = ln.lane & 15;
@@ -397,24 +410,23 @@ __global__ __launch_bounds__(256, 1) void prefix_splitkv_kernel(PrefixArgs a) {
   prime(lds0);
   int t = 0;                 // tile held by the buffer processed next
   bool restart = false;      // workgroup-uniform
+  bool have_ref = false;     // workgroup-uniform: the reference m is set
   // one tile: `cur` holds tile t while `nxt` receives tile t+1
   auto half_step = [&](uint8_t* cur, uint8_t* nxt) -> bool {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (restart) {
-      restart = false;
+      restart = false;                 // tile_math has cleared o and l
       t = 0;
-#pragma unroll
-      for (int d = 0; d < 8; ++d) o[d] = f32x16{};
-      st.l = 0.f;
       prime(cur);
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
     } else if (t >= ntiles) {
       return false;
     }
-    restart = tile_math(cur, x, qf, o, st, min(kKeyTile, kend - kbeg - t * kKeyTile), a.scale_log2, ln, a.pool,
-                        sl_next, nxt);
+    restart = tile_math(cur, x, qf, o, st, !have_ref, min(kKeyTile, kend - kbeg - t * kKeyTile), a.scale_log2, ln,
+                        a.pool, sl_next, nxt);
+    have_ref = true;
     // slots of tile t+2; their latency hides under the wait for tile t+1
     sl_next = load_slots(t + 2);
     ++t;
@@ -426,7 +438,7 @@ __global__ __launch_bounds__(256, 1) void prefix_splitkv_kernel(PrefixArgs a) {
   }
 
   // row sum: own lane, lane ^ 32, and the partner's two lanes
-  const float lpair = st.l + __shfl_xor(st.l, 32);
+  const float lpair = sum_xor32(st.l);
   lds_barrier();                      // everyone is done reading the last P exchange
   x.v[ln.w][0][ln.lane] = make_float4(lpair, 0.f, 0.f, 0.f);
   lds_barrier();
