@@ -76,9 +76,10 @@ constexpr int kPrePV = 4;           // same for PV (two transposed reads each)
 constexpr int kQkSteps = kDqk / 16; // 36 MFMA steps over the query columns
 
 // Which gather instruction of the next tile (0..17, or -1 for none) rides
-// along with QK step i (0..35).  Issuing them spread out keeps the wave from
-// stalling on a full address queue.
-__device__ __forceinline__ constexpr int qk_dma(int i) { return (i & 1) == 0 ? (i >> 1) : -1; }
+// along with MFMA step g of a tile (QK steps 0..35, then PV steps 36..67).
+// Issuing them spread out keeps the wave from stalling on a full address
+// queue.
+__device__ __forceinline__ constexpr int dma_at(int g) { return (g < 36 && (g & 1) == 0) ? (g >> 1) : -1; }
 // Buffer descriptor word 3 for plain dword loads (32-bit data format, no swizzle)
 constexpr int kRsrcWord3 = 0x00020000;
 
@@ -223,30 +224,6 @@ __device__ __forceinline__ void pack_p(const f32x16& v, float scale, float m, bf
   }
 }
 
-// O^T += V^T P^T over key block kb (two 16-key MFMA steps) for this wave's
-// 256 output columns; the eight column blocks interleave so consecutive MFMAs
-// are independent.  P keeps the key order of the score accumulator layout,
-// and the transposed V reads take the keys in that same order.
-__device__ __forceinline__ void pv_block(const uint8_t* lds, const Lane& ln, int kb, const bf16x8 (&p)[2],
-                                         f32x16 (&o)[8]) {
-  const int b0 = ln.pv[0] + kb * 32768, b1 = ln.pv[1] + kb * 32768;
-  auto vfrag = [&](int i) {   // i = half*8 + j
-    const int j = i & 7, half = i >> 3;
-    const int off = half * 16 * 1024 + (j >> 2) * 256;
-    return tr_pair(lds, xor_at_use(b0, 64 * (j & 3)) + off, xor_at_use(b1, 64 * (j & 3)) + off);
-  };
-  bf16x8 vf[kPrePV];
-#pragma unroll
-  for (int i = 0; i < kPrePV; ++i) vf[i] = vfrag(i);
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const bf16x8 cur = vf[i % kPrePV];
-    if (i + kPrePV < 16) vf[i % kPrePV] = vfrag(i + kPrePV);
-    o[i & 7] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur, p[i >> 3], o[i & 7], 0, 0, 0);
-    __builtin_amdgcn_sched_barrier(0);
-  }
-}
-
 // One staged 64-key tile for this wave.  `first` (workgroup-uniform): the
 // chunk's reference m is not set yet.  Returns true when the workgroup must
 // restart its chunk; the tile's contribution is then discarded.
@@ -268,7 +245,7 @@ __device__ __forceinline__ bool tile_math(const uint8_t* lds, Xchg& x, const bf1
       if (i & 1) sp1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur, qf[i], sp1, 0, 0, 0);
       else sp0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur, qf[i], sp0, 0, 0, 0);
       // on a chunk's last tile the gather refetches valid rows into the idle buffer
-      if (qk_dma(i) >= 0) gather_one(pool, ng_sl, ng_lds, ln.w, ln.lane, qk_dma(i));
+      if (dma_at(i) >= 0) gather_one(pool, ng_sl, ng_lds, ln.w, ln.lane, dma_at(i));
       __builtin_amdgcn_sched_barrier(0);
     }
   }
@@ -296,9 +273,43 @@ __device__ __forceinline__ bool tile_math(const uint8_t* lds, Xchg& x, const bf1
   x.v[ln.w][0][ln.lane] = __builtin_bit_cast(float4, pb[0]);
   x.v[ln.w][1][ln.lane] = __builtin_bit_cast(float4, pb[1]);
   x.v[ln.w][2][ln.lane] = make_float4(mt, want, 0.f, 0.f);
-  pv_block(lds, ln, ln.hf, pb, o);                  // discarded if the chunk restarts
-  lds_barrier();
-  // every wave stored its wave-uniform vote in all lanes, so read at own lane
+  // O^T += V^T P^T for this wave's 256 output columns: steps 0..15 over its
+  // own key block, steps 16..31 over the partner's, whose P arrives through
+  // LDS behind the tile's barrier.  The eight column blocks interleave so
+  // consecutive MFMAs are independent; P keeps the key order of the score
+  // accumulator layout and the transposed V reads take the keys in that same
+  // order.  The V reads run kPrePV steps ahead, across the barrier.
+  {
+    const int own0 = ln.pv[0] + ln.hf * 32768, own1 = ln.pv[1] + ln.hf * 32768;
+    const int oth0 = own0 ^ 32768, oth1 = own1 ^ 32768;
+    auto vfrag = [&](int i) {
+      const int j = i & 7, half = (i >> 3) & 1;
+      const int off = half * 16 * 1024 + (j >> 2) * 256;
+      const int b0 = i < 16 ? own0 : oth0, b1 = i < 16 ? own1 : oth1;
+      return tr_pair(lds, xor_at_use(b0, 64 * (j & 3)) + off, xor_at_use(b1, 64 * (j & 3)) + off);
+    };
+    bf16x8 pq[2];
+    bf16x8 vf[kPrePV];
+#pragma unroll
+    for (int i = 0; i < kPrePV; ++i) vf[i] = vfrag(i);
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      if (i == 16) {
+        lds_barrier();
+        pq[0] = __builtin_bit_cast(bf16x8, x.v[ln.w ^ 1][0][ln.lane]);
+        pq[1] = __builtin_bit_cast(bf16x8, x.v[ln.w ^ 1][1][ln.lane]);
+      }
+      const bf16x8 cur = vf[i % kPrePV];
+      if (i + kPrePV < 32) vf[i % kPrePV] = vfrag(i + kPrePV);
+      const bf16x8 bop = i < 16 ? pb[(i >> 3) & 1] : pq[(i >> 3) & 1];
+      o[i & 7] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur, bop, o[i & 7], 0, 0, 0);
+      if (dma_at(36 + i) >= 0) gather_one(pool, ng_sl, ng_lds, ln.w, ln.lane, dma_at(36 + i));
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  // The restart vote is read only now: a restarting chunk discards this
+  // tile's accumulation anyway.  Every wave stored its wave-uniform vote in
+  // all lanes, so each lane reads its own.
   const float any_flag = x.v[0][2][ln.lane].y + x.v[1][2][ln.lane].y + x.v[2][2][ln.lane].y + x.v[3][2][ln.lane].y;
   if (__builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, any_flag)) != 0) {
     // a score ran past the reference: restart the chunk with headroom
@@ -310,9 +321,6 @@ __device__ __forceinline__ bool tile_math(const uint8_t* lds, Xchg& x, const bf1
     return true;
   }
   st.l += lsum;
-  const bf16x8 pq[2] = {__builtin_bit_cast(bf16x8, x.v[ln.w ^ 1][0][ln.lane]),
-                        __builtin_bit_cast(bf16x8, x.v[ln.w ^ 1][1][ln.lane])};
-  pv_block(lds, ln, ln.hf ^ 1, pq, o);
   return false;
 }
 
