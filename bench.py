@@ -155,11 +155,8 @@ def main():
     def step(i):
         vb.verify_attn_mla(prob, q, pools[i % n_copies], pre, tre, par, cup, cut, ws=ws, out=out, lse=lse)
 
-    def prefix_only(i):
-        vb.prefix_partials(prob, q, pools[i % n_copies], pre, cup, cut, ws)
-
-    def tail_only(i):
-        vb.tree_tail(prob, q, pools[i % n_copies], tre, par, cup, cut, ws)
+    def split_only(i):
+        vb.split_partials(prob, q, pools[i % n_copies], pre, tre, par, cup, cut, ws)
 
     def merge_only(i):
         vb.lse_merge(prob, cup, cut, ws, out, lse)
@@ -180,14 +177,14 @@ def main():
 
     # --- per-kernel durations (HIP events on the launch stream) ---
     iters = max(20, min(args.steps, 200))
-    ms_prefix = time_events(prefix_only, iters)
-    ms_tail = time_events(tail_only, iters)
+    ms_split = time_events(split_only, iters)
     ms_merge = time_events(merge_only, iters)
     ms_step_ev = time_events(step, iters)
-    achieved = alg["prefix_flops"] / (ms_prefix * 1e-3) / 1e12
+    # algorithmic flops of the split kernel: every (row, visible key) pair, prefix and tree
+    achieved = (alg["prefix_flops"] + alg["tail_flops"]) / (ms_split * 1e-3) / 1e12
     err(f"[bench] step {ms_per_step * 1e3:.1f} us (wall), {ms_step_ev * 1e3:.1f} us (events); "
-        f"prefix {ms_prefix * 1e3:.1f} us, tail {ms_tail * 1e3:.1f} us, merge {ms_merge * 1e3:.1f} us")
-    err(f"[bench] prefix kernel {achieved:.1f} TFLOP/s = {achieved / MFMA_BF16_PEAK_TFLOPS * 100:.1f}% of bf16 "
+        f"split {ms_split * 1e3:.1f} us, merge {ms_merge * 1e3:.1f} us")
+    err(f"[bench] split kernel {achieved:.1f} TFLOP/s = {achieved / MFMA_BF16_PEAK_TFLOPS * 100:.1f}% of bf16 "
         f"MFMA peak; effective KV {value:.1f} GB/s = {value / HBM_PEAK_GBS * 100:.2f}% of HBM peak")
     t_mfma = (alg["prefix_flops"] + alg["tail_flops"]) / (MFMA_BF16_PEAK_TFLOPS * 1e12)
     t_hbm = (alg["kv_bytes"] + alg["io_bytes"]) / (HBM_PEAK_GBS * 1e9)
@@ -227,8 +224,7 @@ def main():
             "pool_slots": int(x.pool.shape[0]), "kv_bytes": alg["kv_bytes"],
             "us_per_step": round(ms_per_step * 1e3, 2),
             "pct_hbm_peak": round(value / HBM_PEAK_GBS * 100, 3),
-            "kernel_us": {"prefix_splitkv": round(ms_prefix * 1e3, 2), "tree_tail": round(ms_tail * 1e3, 2),
-                          "lse_merge": round(ms_merge * 1e3, 2)},
+            "kernel_us": {"prefix_splitkv": round(ms_split * 1e3, 2), "lse_merge": round(ms_merge * 1e3, 2)},
             "binding_roofline_fraction": round(max(t_mfma, t_hbm) / (ms_per_step * 1e-3), 4),
         },
         "roofline": {

@@ -20,7 +20,9 @@
  *     DDTree Verification", "The Message in Full": the prefix is attended densely
  *     by every node with no causal constraint (causal=False, cache_seqlens=L);
  *     RoPE is applied upstream; num_heads_k=1, head_dim=576; the work splits into
- *     a dense prefix pass, a small masked tree-tail pass and a merge of the two.
+ *     a dense prefix part, a small masked tree-tail part and a merge.  Here the
+ *     tree tail rides along with the last prefix chunk of each request, so the
+ *     split pass leaves one partial per chunk and the merge combines those.
  *   - "The Anatomy of a Kernel Investigation", "The Reasoning Process: A Deep
  *     Dive", Phase 2: the split-KV design merged through the log-sum-exp of
  *     partial attention states.
@@ -105,12 +107,10 @@ typedef struct vamla_plan_info {
   int32_t chunk;            /* prefix keys per split (multiple of 64) */
   int32_t row_tiles;        /* ceil(max_tree * H / 64): row tiles per request */
   int32_t max_chunks;       /* ceil(max_prefix / chunk), >= 1 */
-  int32_t grid_items;       /* prefix kernel grid (B * row_tiles * max_chunks, padded to 8) */
+  int32_t grid_items;       /* split kernel grid (B * row_tiles * max_chunks, padded to 8) */
   /* workspace layout (byte offsets from vamla_params.workspace) */
   size_t off_part_o;        /* float [B][row_tiles][max_chunks][128 d4][64 rows][4] */
   size_t off_part_lse;      /* float [B][row_tiles][max_chunks][64 rows] */
-  size_t off_tail_o;        /* float [B][row_tiles][128 d4][64 rows][4] */
-  size_t off_tail_lse;      /* float [B][row_tiles][64 rows] */
   size_t workspace_bytes;   /* total */
 } vamla_plan_info;
 
@@ -143,8 +143,9 @@ int vamla_validate(const vamla_params* p, const int32_t* h_parent, const int32_t
                    const int32_t* h_tree_slot_idx);
 
 /*
- * The verify step: prefix split-KV pass, masked tree-tail pass and LSE merge,
- * three kernels enqueued on `stream`.
+ * The verify step: the split pass (prefix chunks; the last chunk of each
+ * request also takes its tree keys under the ancestor mask) and the LSE merge,
+ * two kernels enqueued on `stream`.
  *   q               device bf16 [T, H, 576]: queries of every node (RoPE applied)
  *   kv_pool         device bf16 [P, 576]: latent rows; V = first 512 columns
  *   prefix_slot_idx device int32 [total_prefix]: pool slot of each prefix token
@@ -162,28 +163,26 @@ int verify_attn_mla(const vamla_params* p, const uint16_t* q, const uint16_t* kv
                     const int32_t* parent, uint16_t* out, float* lse, void* stream);
 
 /*
- * Stage 1 alone: split-KV attention of every row over each prefix chunk,
- * written to the workspace (part_o normalised by its own softmax sum, part_lse
- * natural log; layout in vamla_plan_info).  Chunk s of request b covers prefix
- * tokens [s*chunk, min((s+1)*chunk, L_b)); chunks at or past L_b are not written.
- * Split-KV design: "The Anatomy of a Kernel Investigation", Phase 2.
+ * Stage 1 alone: split-KV attention of every row over each chunk of its
+ * request's prefix, written to the workspace (part_o normalised by its own
+ * softmax sum, part_lse natural log; layout in vamla_plan_info).  Chunk s of
+ * request b covers prefix tokens [s*chunk, min((s+1)*chunk, L_b)); the last
+ * chunk, s = max(1, ceil(L_b/chunk)) - 1, also covers the request's tree keys,
+ * each row seeing the keys of its node's ancestors and itself.  Chunks past
+ * that are not written.  Arguments as for verify_attn_mla.  Split-KV design:
+ * "The Anatomy of a Kernel Investigation", Phase 2; the masked tree keys:
+ * "Mapping the Optimization Landscape ...", "Input Knowledge Required to
+ * Understand This Message", item 1.
  */
-int vamla_prefix_partials(const vamla_params* p, const uint16_t* q, const uint16_t* kv_pool,
-                          const int32_t* prefix_slot_idx, void* stream);
+int vamla_split_partials(const vamla_params* p, const uint16_t* q, const uint16_t* kv_pool,
+                         const int32_t* prefix_slot_idx, const int32_t* tree_slot_idx, const int32_t* parent,
+                         void* stream);
 
 /*
- * Stage 2 alone: attention of every row over its own tree keys under the
- * ancestor-or-self mask, written to the workspace tail slots.  "The Architecture
- * Detective ...", "The Message in Full": the small masked tree-tail pass.
- */
-int vamla_tree_tail(const vamla_params* p, const uint16_t* q, const uint16_t* kv_pool,
-                    const int32_t* tree_slot_idx, const int32_t* parent, void* stream);
-
-/*
- * Stage 3 alone: merges the prefix chunk partials and the tail partial in the
- * workspace into out (bf16) and lse (float): lse = ln sum_s exp(lse_s),
- * out = sum_s exp(lse_s - lse) * o_s.  Same pages: merging partial attention
- * states by their log-sum-exp.
+ * Stage 2 alone: merges the chunk partials in the workspace into out (bf16)
+ * and lse (float): lse = ln sum_s exp(lse_s), out = sum_s exp(lse_s - lse) * o_s
+ * over the max(1, ceil(L_b/chunk)) partials of each request.  Same pages:
+ * merging partial attention states by their log-sum-exp.
  */
 int vamla_lse_merge(const vamla_params* p, uint16_t* out, float* lse, void* stream);
 

@@ -31,7 +31,7 @@ STATUS = {
 }
 
 EXPORTS = ("vamla_status_string", "vamla_plan", "vamla_workspace_size", "vamla_validate", "verify_attn_mla",
-           "vamla_prefix_partials", "vamla_tree_tail", "vamla_lse_merge", "vamla_slot_gather")
+           "vamla_split_partials", "vamla_lse_merge", "vamla_slot_gather")
 
 
 class VamlaParams(ctypes.Structure):
@@ -63,8 +63,6 @@ class VamlaPlanInfo(ctypes.Structure):
         ("grid_items", ctypes.c_int32),
         ("off_part_o", ctypes.c_size_t),
         ("off_part_lse", ctypes.c_size_t),
-        ("off_tail_o", ctypes.c_size_t),
-        ("off_tail_lse", ctypes.c_size_t),
         ("workspace_bytes", ctypes.c_size_t),
     ]
 
@@ -94,8 +92,7 @@ def lib() -> ctypes.CDLL:
     L.vamla_workspace_size.argtypes = [P(VamlaParams), P(ctypes.c_size_t)]
     L.vamla_validate.argtypes = [P(VamlaParams), vp, vp, vp, vp, vp]
     L.verify_attn_mla.argtypes = [P(VamlaParams), vp, vp, vp, vp, vp, vp, vp, vp]
-    L.vamla_prefix_partials.argtypes = [P(VamlaParams), vp, vp, vp, vp]
-    L.vamla_tree_tail.argtypes = [P(VamlaParams), vp, vp, vp, vp, vp]
+    L.vamla_split_partials.argtypes = [P(VamlaParams), vp, vp, vp, vp, vp, vp]
     L.vamla_lse_merge.argtypes = [P(VamlaParams), vp, vp, vp]
     L.vamla_slot_gather.argtypes = [vp, vp, i64, vp, vp]
     for name in EXPORTS:
@@ -258,17 +255,14 @@ def verify_attn_mla(prob: Problem, q, kv_pool, prefix_slot_idx, tree_slot_idx, p
     return out, lse
 
 
-def prefix_partials(prob: Problem, q, kv_pool, prefix_slot_idx, cu_prefix, cu_tree, ws: Workspace, stream=None):
+def split_partials(prob: Problem, q, kv_pool, prefix_slot_idx, tree_slot_idx, parent, cu_prefix, cu_tree,
+                   ws: Workspace, stream=None):
+    """Stage 1: chunk partials into the workspace (the last chunk of each
+    request also covers its tree keys)."""
     p = _params(prob, cu_prefix, cu_tree, ws)
-    _check(lib().vamla_prefix_partials(ctypes.byref(p), _ptr(_bits(q, "q")), _ptr(_bits(kv_pool, "kv_pool")),
-                                       _ptr(prefix_slot_idx) if prob.total_prefix else None, _stream(stream)),
-           "vamla_prefix_partials")
-
-
-def tree_tail(prob: Problem, q, kv_pool, tree_slot_idx, parent, cu_prefix, cu_tree, ws: Workspace, stream=None):
-    p = _params(prob, cu_prefix, cu_tree, ws)
-    _check(lib().vamla_tree_tail(ctypes.byref(p), _ptr(_bits(q, "q")), _ptr(_bits(kv_pool, "kv_pool")),
-                                 _ptr(tree_slot_idx), _ptr(parent), _stream(stream)), "vamla_tree_tail")
+    _check(lib().vamla_split_partials(ctypes.byref(p), _ptr(_bits(q, "q")), _ptr(_bits(kv_pool, "kv_pool")),
+                                      _ptr(prefix_slot_idx) if prob.total_prefix else None, _ptr(tree_slot_idx),
+                                      _ptr(parent), _stream(stream)), "vamla_split_partials")
 
 
 def lse_merge(prob: Problem, cu_prefix, cu_tree, ws: Workspace, out, lse, stream=None):
@@ -289,8 +283,8 @@ def slot_gather(kv_pool, idx, dst=None, stream=None):
 
 def workspace_views(prob: Problem, ws: Workspace):
     """Typed views of the workspace regions (for stage-level checks):
-    part_o [B, tiles, chunks, 128, 64, 4], part_lse [B, tiles, chunks, 64],
-    tail_o [B, tiles, 128, 64, 4], tail_lse [B, tiles, 64] (all float32)."""
+    part_o [B, tiles, chunks, 128, 64, 4], part_lse [B, tiles, chunks, 64]
+    (float32)."""
     torch = _torch()
     info = plan(prob)
     B, R, C = prob.batch, info.row_tiles, info.max_chunks
@@ -303,6 +297,4 @@ def workspace_views(prob: Problem, ws: Workspace):
         return f[off // 4: off // 4 + n].view(*shape)
     return dict(plan=info,
                 part_o=region(info.off_part_o, (B, R, C, D_V // 4, ROW_TILE, 4)),
-                part_lse=region(info.off_part_lse, (B, R, C, ROW_TILE)),
-                tail_o=region(info.off_tail_o, (B, R, D_V // 4, ROW_TILE, 4)),
-                tail_lse=region(info.off_tail_lse, (B, R, ROW_TILE)))
+                part_lse=region(info.off_part_lse, (B, R, C, ROW_TILE)))

@@ -18,11 +18,13 @@ constexpr int kTileBytes = kChunks16 * kKeyTile * 16;   // 73728 B of LDS per ke
 constexpr int kMaxTree = 65;
 constexpr int kMaxHeads = 128;
 
-// Prefix split-KV pass.
+// Split-KV pass: prefix chunks, the last one of each request with its tree keys.
 struct PrefixArgs {
   const uint16_t* q;          // [T, H, 576] bf16
   const uint16_t* pool;       // [P, 576] bf16
   const int32_t* prefix_slot; // [total_prefix]
+  const int32_t* tree_slot;   // [T]
+  const int32_t* parent;      // [T], request-local
   const int32_t* cu_prefix;   // [B+1]
   const int32_t* cu_tree;     // [B+1]
   float* part_o;              // [B][row_tiles][max_chunks][128 d4][64 rows][4]
@@ -36,28 +38,10 @@ struct PrefixArgs {
   float scale_log2;           // softmax_scale * log2(e)
 };
 
-// Masked tree-tail pass.
-struct TailArgs {
-  const uint16_t* q;
-  const uint16_t* pool;
-  const int32_t* tree_slot;   // [T]
-  const int32_t* parent;      // [T], request-local
-  const int32_t* cu_tree;     // [B+1]
-  float* tail_o;              // [B][row_tiles][128 d4][64 rows][4]
-  float* tail_lse;            // [B][row_tiles][64 rows]
-  int32_t num_heads;
-  int32_t row_tiles;
-  int32_t batch;
-  int32_t total_tree;
-  float scale;
-};
-
-// LSE merge of prefix chunk partials and the tail partial.
+// LSE merge of the chunk partials.
 struct MergeArgs {
   const float* part_o;
   const float* part_lse;
-  const float* tail_o;
-  const float* tail_lse;
   const int32_t* cu_prefix;
   const int32_t* cu_tree;
   uint16_t* out;              // [T, H, 512] bf16
@@ -70,7 +54,6 @@ struct MergeArgs {
 };
 
 hipError_t launch_prefix_splitkv(const PrefixArgs& a, hipStream_t stream);
-hipError_t launch_tree_tail(const TailArgs& a, hipStream_t stream);
 hipError_t launch_lse_merge(const MergeArgs& a, hipStream_t stream);
 hipError_t launch_slot_gather(const uint16_t* pool, const int32_t* idx, int64_t n, uint16_t* dst,
                               hipStream_t stream);

@@ -1,14 +1,14 @@
 // Log-sum-exp merge of split attention partials (gfx950).
 //
-// The prefix pass leaves one normalised partial (o_s, lse_s) per prefix chunk
-// and the tail pass one (o_tail, lse_tail) per row.  The exact attention over
-// their union is
+// The split pass leaves one normalised partial (o_s, lse_s) per prefix chunk
+// of a request, the last one covering the request's tree keys as well (a
+// request with no prefix has one partial, over its tree).  The exact attention
+// over their union is
 //     lse = ln( sum_s exp(lse_s) ),   out = sum_s exp(lse_s - lse) * o_s,
 // the merge of partial attention states the split design relies on ("The
 // Anatomy of a Kernel Investigation", "The Reasoning Process: A Deep Dive",
 // Phase 2; "The Architecture Detective: ...", "The Message in Full").
-// Chunks past a request's prefix were never written and are not read; a
-// request with no prefix merges the tail alone.
+// Chunks past a request's prefix were never written and are not read.
 //
 // Layout: partials are [item][128 d4][64 rows][4 floats], so thread = row reads
 // coalesced 16-byte pieces; grid = (request x row tile) x column groups.
@@ -31,14 +31,13 @@ __global__ __launch_bounds__(kRowTile) void lse_merge_kernel(MergeArgs a) {
   if (r >= rows_b) return;
   const int L = a.cu_prefix[b + 1] - a.cu_prefix[b];
   // a prefix longer than max_prefix is a caller error; never read past the plan
-  const int S = min((L + a.chunk - 1) / a.chunk, a.max_chunks);
+  const int S = max(1, min((L + a.chunk - 1) / a.chunk, a.max_chunks));
 
   const size_t tb = (size_t)b * a.row_tiles + tile;
   const size_t p0 = tb * a.max_chunks;
-  const float lt = a.tail_lse[tb * kRowTile + rit];
-  float m = lt;
+  float m = -INFINITY;
   for (int s = 0; s < S; ++s) m = fmaxf(m, a.part_lse[(p0 + s) * kRowTile + rit]);
-  float sum = __expf(lt - m);
+  float sum = 0.f;
   for (int s = 0; s < S; ++s) sum += __expf(a.part_lse[(p0 + s) * kRowTile + rit] - m);
   const float lse = m + logf(sum);
 
@@ -47,14 +46,8 @@ __global__ __launch_bounds__(kRowTile) void lse_merge_kernel(MergeArgs a) {
 
   const int d4_0 = blockIdx.y * kD4PerBlock;
   float4 acc[kD4PerBlock];
-  {
-    const float wt = __expf(lt - lse);
 #pragma unroll
-    for (int j = 0; j < kD4PerBlock; ++j) {
-      const float4 v = *(const float4*)(a.tail_o + ((tb * kD4 + d4_0 + j) * kRowTile + rit) * 4);
-      acc[j] = make_float4(wt * v.x, wt * v.y, wt * v.z, wt * v.w);
-    }
-  }
+  for (int j = 0; j < kD4PerBlock; ++j) acc[j] = make_float4(0.f, 0.f, 0.f, 0.f);
   for (int s = 0; s < S; ++s) {
     const float ws = __expf(a.part_lse[(p0 + s) * kRowTile + rit] - lse);
 #pragma unroll

@@ -175,7 +175,7 @@ struct Lane {
   // key = 32*hf + l32 (the lane's key of the wave's block)
   int qk_lat;        // latent: key*1024 | ((hl ^ g(key)) << 4); step s: ^ 32*(s&7), + 256*(s>>3)
   int qk_rope;       // rope: 64K + key*128 | ((hl ^ h(key)) << 4); rope step r: ^ 32*r
-  int pv[2];         // PV transposed reads, key group sec: column block d: ^ 64*(d&3), + 256*(d>>2)
+  int pv[2];         // PV transposed reads, key group sec: column block c: ^ 64*c
 };
 
 struct RowState {
@@ -228,7 +228,8 @@ __device__ __forceinline__ void pack_p(const f32x16& v, float scale, float m, bf
 // chunk's reference m is not set yet.  Returns true when the workgroup must
 // restart its chunk; the tile's contribution is then discarded.
 __device__ __forceinline__ bool tile_math(const uint8_t* lds, Xchg& x, const bf16x8 (&qf)[kQkSteps],
-                                          f32x16 (&o)[8], RowState& st, bool first, int nvalid, float scale_log2,
+                                          f32x16 (&o)[8], RowState& st, bool first, int nvalid, bool masked,
+                                          uint64_t vis, float scale_log2,
                                           const Lane& ln, const uint16_t* pool, const TileSlots& ng_sl,
                                           uint8_t* ng_lds) {
   // S^T of this wave's key block over all 576 columns; even and odd steps
@@ -256,6 +257,11 @@ __device__ __forceinline__ bool tile_math(const uint8_t* lds, Xchg& x, const bf1
     for (int r = 0; r < 16; ++r)
       if (32 * ln.hf + 8 * (r >> 2) + 4 * ln.hl + (r & 3) >= nvalid) v[r] = -INFINITY;
   }
+  if (masked) {       // tree keys: bit k of vis = key k of the tile is visible to this row
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      if (((vis >> (32 * ln.hf + 8 * (r >> 2) + 4 * ln.hl + (r & 3))) & 1) == 0) v[r] = -INFINITY;
+  }
   float mt = v[0];
 #pragma unroll
   for (int r = 1; r < 16; ++r) mt = fmaxf(mt, v[r]);
@@ -273,38 +279,53 @@ __device__ __forceinline__ bool tile_math(const uint8_t* lds, Xchg& x, const bf1
   x.v[ln.w][0][ln.lane] = __builtin_bit_cast(float4, pb[0]);
   x.v[ln.w][1][ln.lane] = __builtin_bit_cast(float4, pb[1]);
   x.v[ln.w][2][ln.lane] = make_float4(mt, want, 0.f, 0.f);
-  // O^T += V^T P^T for this wave's 256 output columns: steps 0..15 over its
-  // own key block, steps 16..31 over the partner's, whose P arrives through
-  // LDS behind the tile's barrier.  The eight column blocks interleave so
-  // consecutive MFMAs are independent; P keeps the key order of the score
+  // O^T += V^T P^T for this wave's 128 output columns [128w, 128w+128) over
+  // all 64 rows and all 64 keys.  P of the four (row block, key block) pairs
+  // comes from the four waves: this wave's from registers, the rest from LDS
+  // behind the tile's barrier.  Each V^T fragment (32 columns x 16 keys) feeds
+  // the MFMAs of both row blocks.  P keeps the key order of the score
   // accumulator layout and the transposed V reads take the keys in that same
-  // order.  The V reads run kPrePV steps ahead, across the barrier.
+  // order.  Key steps ks = 2*kb' + h run over the own key block (kb' = 0)
+  // first; o[4*rb' + c] accumulates column block c of row block rb' (rb' = 0:
+  // this pair's rows).
   {
     const int own0 = ln.pv[0] + ln.hf * 32768, own1 = ln.pv[1] + ln.hf * 32768;
     const int oth0 = own0 ^ 32768, oth1 = own1 ^ 32768;
-    auto vfrag = [&](int i) {
-      const int j = i & 7, half = (i >> 3) & 1;
-      const int off = half * 16 * 1024 + (j >> 2) * 256;
-      const int b0 = i < 16 ? own0 : oth0, b1 = i < 16 ? own1 : oth1;
-      return tr_pair(lds, xor_at_use(b0, 64 * (j & 3)) + off, xor_at_use(b1, 64 * (j & 3)) + off);
+    auto vfrag = [&](int ks, int c) {
+      const int off = (ks & 1) * 16 * 1024;
+      const int b0 = ks < 2 ? own0 : oth0, b1 = ks < 2 ? own1 : oth1;
+      return tr_pair(lds, xor_at_use(b0, 64 * c) + off, xor_at_use(b1, 64 * c) + off);
     };
-    bf16x8 pq[2];
-    bf16x8 vf[kPrePV];
+    bf16x8 vf[4];
 #pragma unroll
-    for (int i = 0; i < kPrePV; ++i) vf[i] = vfrag(i);
+    for (int c = 0; c < 4; ++c) vf[c] = vfrag(0, c);
+    lds_barrier();
+    // P operands of the other waves, read as the key steps reach them:
+    // (this pair's rows, other key block) from w^1, (other rows, own block)
+    // from w^2, (other rows, other block) from w^3
+    auto pfrom = [&](int wv, int h) { return __builtin_bit_cast(bf16x8, x.v[wv][h][ln.lane]); };
+    bf16x8 q0n = pb[0], q1n = pfrom(ln.w ^ 2, 0);
 #pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      if (i == 16) {
-        lds_barrier();
-        pq[0] = __builtin_bit_cast(bf16x8, x.v[ln.w ^ 1][0][ln.lane]);
-        pq[1] = __builtin_bit_cast(bf16x8, x.v[ln.w ^ 1][1][ln.lane]);
+    for (int ks = 0; ks < 4; ++ks) {
+      const bf16x8 q0 = q0n;                           // this pair's rows
+      const bf16x8 q1 = q1n;                           // the other pair's rows
+      if (ks < 3) {
+        const int n = ks + 1, h = n & 1;
+        q0n = n < 2 ? pb[h] : pfrom(ln.w ^ 1, h);
+        q1n = pfrom(n < 2 ? ln.w ^ 2 : ln.w ^ 3, h);
       }
-      const bf16x8 cur = vf[i % kPrePV];
-      if (i + kPrePV < 32) vf[i % kPrePV] = vfrag(i + kPrePV);
-      const bf16x8 bop = i < 16 ? pb[(i >> 3) & 1] : pq[(i >> 3) & 1];
-      o[i & 7] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur, bop, o[i & 7], 0, 0, 0);
-      if (dma_at(36 + i) >= 0) gather_one(pool, ng_sl, ng_lds, ln.w, ln.lane, dma_at(36 + i));
-      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        o[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[c], q0, o[c], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        o[4 + c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[c], q1, o[4 + c], 0, 0, 0);
+        if (ks < 3) vf[c] = vfrag(ks + 1, c);
+        if (dma_at(36 + 8 * ks + 4 + c) >= 0) gather_one(pool, ng_sl, ng_lds, ln.w, ln.lane, dma_at(36 + 8 * ks + 4 + c));
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
   }
   // The restart vote is read only now: a restarting chunk discards this
@@ -328,6 +349,8 @@ __global__ __launch_bounds__(256, 1) void prefix_splitkv_kernel(PrefixArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t lds0[kTileBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t lds1[kTileBytes];
   __shared__ Xchg x;
+  __shared__ int par_s[kMaxTree];                 // the request's parent array
+  __shared__ uint64_t vis_s[kRowTile][2];         // per row: visible tree keys 0..63, 64..127
 
   Lane ln;
   ln.lane = threadIdx.x & 63;
@@ -349,12 +372,21 @@ __global__ __launch_bounds__(256, 1) void prefix_splitkv_kernel(PrefixArgs a) {
   const int tile = rem - s * a.row_tiles;
   const int p0 = a.cu_prefix[b];
   const int L = a.cu_prefix[b + 1] - p0;
+  // chunks of this request; with no prefix, chunk 0 still carries the tree
+  const int nchunks = max(1, min((L + a.chunk - 1) / a.chunk, a.max_chunks));
+  if (s >= nchunks) return;
   const int kbeg = s * a.chunk;
-  if (kbeg >= L) return;
   const int kend = min(kbeg + a.chunk, L);
   const int t0 = a.cu_tree[b];
-  const int rows_b = (a.cu_tree[b + 1] - t0) * a.num_heads;
+  const int n_b = a.cu_tree[b + 1] - t0;
+  const int rows_b = n_b * a.num_heads;
   if (tile * kRowTile >= rows_b) return;
+  // The request's last chunk also takes its tree keys (<= 65, so at most two
+  // tiles) under the ancestor-or-self mask ("Mapping the Optimization
+  // Landscape for DDTree Verify Attention", "Input Knowledge Required to
+  // Understand This Message", item 1): one partial then covers both.
+  const int ntp = kend > kbeg ? (kend - kbeg + kKeyTile - 1) / kKeyTile : 0;   // prefix tiles
+  const int ntt = s == nchunks - 1 ? (min(n_b, kMaxTree) + kKeyTile - 1) / kKeyTile : 0;   // tree tiles
 
   const int row_in_tile = ln.pr * 32 + ln.l32;
   const int row = tile * kRowTile + row_in_tile;
@@ -383,34 +415,60 @@ __global__ __launch_bounds__(256, 1) void prefix_splitkv_kernel(PrefixArgs a) {
     const int key = 32 * ln.hf + ln.l32;
     ln.qk_lat = (key * 1024) | ((ln.hl ^ swz_latent(key)) << 4);
     ln.qk_rope = (kRopeBase + key * 128) | ((ln.hl ^ swz_rope(key)) << 4);
-    // PV: lane (block gb, sub-lane sl) reads keys kb*32 + half*16 + 4*hl + (sl >> 2) (+8*sec),
-    // columns 32*D + 16*(gb & 1) + 4*(sl & 3) .. +3 of output block D = 8*hf + j
+    // PV: lane (block gb, sub-lane sl) reads keys kb*32 + h*16 + 4*hl + (sl >> 2) (+8*sec),
+    // columns 128w + 32c + 16*(gb & 1) + 4*(sl & 3) .. +3 for column block c
     const int gb = ln.lane >> 4, sl = ln.lane & 15;
     const int kk = 4 * ln.hl + (sl >> 2);
     const int cp = 2 * (gb & 1) + ((sl >> 1) & 1);
 #pragma unroll
     for (int sec = 0; sec < 2; ++sec) {
       const int gk = ((sl >> 2) << 2) | (ln.hl + 2 * sec);   // g(key) of key kk + 8*sec
-      ln.pv[sec] = ((kk + 8 * sec) * 1024 + 512 * ln.hf + 8 * (sl & 1)) | ((cp ^ gk) << 4);
+      ln.pv[sec] = ((kk + 8 * sec) * 1024 + 256 * ln.w + 8 * (sl & 1)) | ((cp ^ gk) << 4);
     }
   }
 
   // Slots of this wave's keys of tile t, one vector load per lane (see
   // TileSlots); keys past the end of the chunk take the last key's slot (a
   // valid index; masked in the math).
-  const int* slots = a.prefix_slot + p0;
-  const int ntiles = (kend - kbeg + kKeyTile - 1) / kKeyTile;
+  const int ntiles = ntp + ntt;
   auto load_slots = [&](int t) {
-    const int base = kbeg + t * kKeyTile + 16 * ln.w;
+    // prefix tiles first, then tree tiles; keys past the end of either list
+    // take its last slot; a tile index past the last tile re-reads it
+    t = min(t, ntiles - 1);
+    const bool tree = t >= ntp;
+    const int* list = tree ? a.tree_slot + t0 : a.prefix_slot + p0;
+    const int base = (tree ? (t - ntp) * kKeyTile : kbeg + t * kKeyTile) + 16 * ln.w;
+    const int last = tree ? min(n_b, kMaxTree) - 1 : kend - 1;
     TileSlots r;
-    r.lat = (uint32_t)slots[min(base + (ln.lane & 15), kend - 1)];
-    r.rope[0] = (uint32_t)slots[min(base + (ln.lane >> 3), kend - 1)];
-    r.rope[1] = (uint32_t)slots[min(base + 8 + (ln.lane >> 3), kend - 1)];
+    r.lat = (uint32_t)list[min(base + (ln.lane & 15), last)];
+    r.rope[0] = (uint32_t)list[min(base + (ln.lane >> 3), last)];
+    r.rope[1] = (uint32_t)list[min(base + 8 + (ln.lane >> 3), last)];
     return r;
   };
 
+  if (ntt > 0) {
+    // Ancestor-or-self sets of this tile's rows as bit masks over the tree
+    // keys.  A parent that does not precede its child ends a walk, so a
+    // malformed array cannot loop; rows past the request's nodes see the root.
+    for (int i = threadIdx.x; i < min(n_b, kMaxTree); i += blockDim.x) par_s[i] = a.parent[t0 + i];
+    __syncthreads();
+    if (threadIdx.x < kRowTile) {
+      const int r = tile * kRowTile + (int)threadIdx.x;
+      int j = r < rows_b ? min(r / a.num_heads, min(n_b, kMaxTree) - 1) : 0;
+      uint64_t m0 = 0, m1 = 0;
+      for (int step = 0; step < kMaxTree && j >= 0; ++step) {
+        if (j < 64) m0 |= 1ull << j; else m1 |= 1ull << (j - 64);
+        const int p = par_s[j];
+        j = (p < j) ? p : -1;
+      }
+      vis_s[threadIdx.x][0] = m0;
+      vis_s[threadIdx.x][1] = m1;
+    }
+    // made visible by the barrier that starts the first tile
+  }
+
   TileSlots sl_next;
-  // put tile 0 into `buf` (chunk start and restarts)
+  // put tile 0 into `buf` (item start and restarts)
   auto prime = [&](uint8_t* buf) {
     gather_tile(a.pool, load_slots(0), buf, ln.w, ln.lane);
     sl_next = load_slots(1);
@@ -432,8 +490,10 @@ __global__ __launch_bounds__(256, 1) void prefix_splitkv_kernel(PrefixArgs a) {
     } else if (t >= ntiles) {
       return false;
     }
-    restart = tile_math(cur, x, qf, o, st, !have_ref, min(kKeyTile, kend - kbeg - t * kKeyTile), a.scale_log2, ln,
-                        a.pool, sl_next, nxt);
+    const bool tree = t >= ntp;
+    const int nvalid = tree ? kKeyTile : min(kKeyTile, kend - kbeg - t * kKeyTile);
+    const uint64_t vis = tree ? vis_s[row_in_tile][t - ntp] : ~0ull;
+    restart = tile_math(cur, x, qf, o, st, !have_ref, nvalid, tree, vis, a.scale_log2, ln, a.pool, sl_next, nxt);
     have_ref = true;
     // slots of tile t+2; their latency hides under the wait for tile t+1
     sl_next = load_slots(t + 2);
@@ -445,28 +505,35 @@ __global__ __launch_bounds__(256, 1) void prefix_splitkv_kernel(PrefixArgs a) {
     if (!half_step(lds1, lds0)) break;
   }
 
-  // row sum: own lane, lane ^ 32, and the partner's two lanes
+  // Row sums and references of both row blocks: this wave holds l over its
+  // key block for this pair's rows; the partner holds the other key block,
+  // the other pair the other rows.
   const float lpair = sum_xor32(st.l);
-  lds_barrier();                      // everyone is done reading the last P exchange
-  x.v[ln.w][0][ln.lane] = make_float4(lpair, 0.f, 0.f, 0.f);
+  lds_barrier();                      // everyone is done reading the last P operands
+  x.v[ln.w][0][ln.lane] = make_float4(lpair, st.m, 0.f, 0.f);
   lds_barrier();
-  const float l_tot = lpair + x.v[ln.w ^ 1][0][ln.lane].x;
-  if (!row_ok) return;
-  const float inv = 1.0f / l_tot;
+  const float4 e1 = x.v[ln.w ^ 1][0][ln.lane], e2 = x.v[ln.w ^ 2][0][ln.lane], e3 = x.v[ln.w ^ 3][0][ln.lane];
+  const float l_rb[2] = {lpair + e1.x, e2.x + e3.x};
   const size_t pidx = ((size_t)b * a.row_tiles + tile) * a.max_chunks + s;
   float* po = a.part_o + pidx * (kD4 * kRowTile * 4);
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int dblk = 8 * ln.hf + j;
+  for (int rb = 0; rb < 2; ++rb) {
+    const int rit = 32 * (ln.pr ^ rb) + ln.l32;
+    if (tile * kRowTile + rit >= rows_b) continue;
+    const float inv = 1.0f / l_rb[rb];
 #pragma unroll
-    for (int rq = 0; rq < 4; ++rq) {
-      const int d4 = dblk * 8 + 2 * rq + ln.hl;
-      float4 v = make_float4(o[j][4 * rq] * inv, o[j][4 * rq + 1] * inv, o[j][4 * rq + 2] * inv,
-                             o[j][4 * rq + 3] * inv);
-      *(float4*)(po + ((size_t)d4 * kRowTile + row_in_tile) * 4) = v;
+    for (int c = 0; c < 4; ++c) {
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq) {
+        const int d4 = (4 * ln.w + c) * 8 + 2 * rq + ln.hl;
+        const f32x16& acc = o[4 * rb + c];
+        const float4 v = make_float4(acc[4 * rq] * inv, acc[4 * rq + 1] * inv, acc[4 * rq + 2] * inv,
+                                     acc[4 * rq + 3] * inv);
+        *(float4*)(po + ((size_t)d4 * kRowTile + rit) * 4) = v;
+      }
     }
   }
-  if (ln.hf == 0 && ln.hl == 0) a.part_lse[pidx * kRowTile + row_in_tile] = st.m * kLn2 + logf(l_tot);
+  if (row_ok && ln.hf == 0 && ln.hl == 0) a.part_lse[pidx * kRowTile + row_in_tile] = st.m * kLn2 + logf(l_rb[0]);
 }
 
 }  // namespace

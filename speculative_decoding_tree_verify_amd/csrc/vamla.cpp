@@ -58,8 +58,10 @@ int64_t choose_chunk(const vamla_params* p, int64_t row_tiles) {
   const int64_t maxL = p->max_prefix;
   if (maxL <= VAMLA_KEY_TILE) return VAMLA_KEY_TILE;
   const int64_t total = p->total_prefix > 0 ? p->total_prefix : maxL;
+  // the last chunk of a request also streams its tree keys (whole tiles)
+  const int64_t tree_keys = ceil_div(p->max_tree, VAMLA_KEY_TILE) * VAMLA_KEY_TILE;
   // Candidates: the longest prefix split into k chunks, k = 1, 2, ...; cost =
-  // rounds of work items over the CUs times the keys each item streams.
+  // rounds of work items over the CUs times the keys the largest item streams.
   int64_t best_c = VAMLA_KEY_TILE, best_cost = INT64_MAX;
   const int64_t kmax = std::min<int64_t>(ceil_div(maxL, VAMLA_KEY_TILE), 8192);
   for (int64_t k = 1; k <= kmax; ++k) {
@@ -69,7 +71,9 @@ int64_t choose_chunk(const vamla_params* p, int64_t row_tiles) {
         std::min<int64_t>(ceil_div(total, c) + (p->batch - 1), (int64_t)p->batch * ceil_div(maxL, c));
     const int64_t items = row_tiles * chunks;
     const int64_t rounds = ceil_div(items, kCUs);
-    const int64_t cost = rounds * (c + kItemOverheadKeys);
+    const int64_t last = maxL - (ceil_div(maxL, c) - 1) * c;
+    const int64_t item_keys = std::max(c, ceil_div(last, VAMLA_KEY_TILE) * VAMLA_KEY_TILE + tree_keys);
+    const int64_t cost = rounds * (item_keys + kItemOverheadKeys);
     if (cost < best_cost || (cost == best_cost && c > best_c)) {   // ties: larger chunk, fewer partials
       best_cost = cost;
       best_c = c;
@@ -100,11 +104,6 @@ int make_plan(const vamla_params* p, vamla_plan_info* out) {
   off = align256(off + (size_t)items * item_o);
   pl.off_part_lse = off;
   off = align256(off + (size_t)items * item_l);
-  const size_t tiles = (size_t)p->batch * row_tiles;
-  pl.off_tail_o = off;
-  off = align256(off + tiles * item_o);
-  pl.off_tail_lse = off;
-  off = align256(off + tiles * item_l);
   pl.workspace_bytes = off;
   *out = pl;
   return VAMLA_OK;
@@ -134,13 +133,15 @@ int workspace_ok(const vamla_params* p, const vamla_plan_info& pl) {
 
 float* ws_f(const vamla_params* p, size_t off) { return (float*)((char*)p->workspace + off); }
 
-int prefix_launch(const vamla_params* p, const vamla_plan_info& pl, const uint16_t* q, const uint16_t* pool,
-                  const int32_t* prefix_slot_idx, hipStream_t stream) {
-  if (p->total_prefix == 0 || p->max_prefix == 0) return VAMLA_OK;   // no prefix keys anywhere
+int split_launch(const vamla_params* p, const vamla_plan_info& pl, const uint16_t* q, const uint16_t* pool,
+                 const int32_t* prefix_slot_idx, const int32_t* tree_slot_idx, const int32_t* parent,
+                 hipStream_t stream) {
   PrefixArgs a;
   a.q = q;
   a.pool = pool;
   a.prefix_slot = prefix_slot_idx;
+  a.tree_slot = tree_slot_idx;
+  a.parent = parent;
   a.cu_prefix = p->cu_prefix;
   a.cu_tree = p->cu_tree;
   a.part_o = ws_f(p, pl.off_part_o);
@@ -155,30 +156,10 @@ int prefix_launch(const vamla_params* p, const vamla_plan_info& pl, const uint16
   return launch_prefix_splitkv(a, stream) == hipSuccess ? VAMLA_OK : VAMLA_ERR_LAUNCH;
 }
 
-int tail_launch(const vamla_params* p, const vamla_plan_info& pl, const uint16_t* q, const uint16_t* pool,
-                const int32_t* tree_slot_idx, const int32_t* parent, hipStream_t stream) {
-  TailArgs a;
-  a.q = q;
-  a.pool = pool;
-  a.tree_slot = tree_slot_idx;
-  a.parent = parent;
-  a.cu_tree = p->cu_tree;
-  a.tail_o = ws_f(p, pl.off_tail_o);
-  a.tail_lse = ws_f(p, pl.off_tail_lse);
-  a.num_heads = p->num_heads;
-  a.row_tiles = pl.row_tiles;
-  a.batch = p->batch;
-  a.total_tree = p->total_tree;
-  a.scale = p->softmax_scale;
-  return launch_tree_tail(a, stream) == hipSuccess ? VAMLA_OK : VAMLA_ERR_LAUNCH;
-}
-
 int merge_launch(const vamla_params* p, const vamla_plan_info& pl, uint16_t* out, float* lse, hipStream_t stream) {
   MergeArgs a;
   a.part_o = ws_f(p, pl.off_part_o);
   a.part_lse = ws_f(p, pl.off_part_lse);
-  a.tail_o = ws_f(p, pl.off_tail_o);
-  a.tail_lse = ws_f(p, pl.off_tail_lse);
   a.cu_prefix = p->cu_prefix;
   a.cu_tree = p->cu_tree;
   a.out = out;
@@ -186,7 +167,6 @@ int merge_launch(const vamla_params* p, const vamla_plan_info& pl, uint16_t* out
   a.num_heads = p->num_heads;
   a.chunk = pl.chunk;
   a.row_tiles = pl.row_tiles;
-  // with no prefix keys anywhere the prefix pass never ran: merge the tail alone
   a.max_chunks = pl.max_chunks;
   a.batch = p->batch;
   return launch_lse_merge(a, stream) == hipSuccess ? VAMLA_OK : VAMLA_ERR_LAUNCH;
@@ -278,30 +258,20 @@ int verify_attn_mla(const vamla_params* p, const uint16_t* q, const uint16_t* kv
   if (!q || !kv_pool || !tree_slot_idx || !parent || !out || !lse) return VAMLA_ERR_INVALID_ARG;
   if (p->total_prefix > 0 && !prefix_slot_idx) return VAMLA_ERR_INVALID_ARG;
   hipStream_t s = (hipStream_t)stream;
-  st = prefix_launch(p, pl, q, kv_pool, prefix_slot_idx, s);
-  if (st != VAMLA_OK) return st;
-  st = tail_launch(p, pl, q, kv_pool, tree_slot_idx, parent, s);
+  st = split_launch(p, pl, q, kv_pool, prefix_slot_idx, tree_slot_idx, parent, s);
   if (st != VAMLA_OK) return st;
   return merge_launch(p, pl, out, lse, s);
 }
 
-int vamla_prefix_partials(const vamla_params* p, const uint16_t* q, const uint16_t* kv_pool,
-                          const int32_t* prefix_slot_idx, void* stream) {
-  vamla_plan_info pl;
-  int st = prologue(p, &pl);
-  if (st != VAMLA_OK) return st;
-  if (!q || !kv_pool) return VAMLA_ERR_INVALID_ARG;
-  if (p->total_prefix > 0 && !prefix_slot_idx) return VAMLA_ERR_INVALID_ARG;
-  return prefix_launch(p, pl, q, kv_pool, prefix_slot_idx, (hipStream_t)stream);
-}
-
-int vamla_tree_tail(const vamla_params* p, const uint16_t* q, const uint16_t* kv_pool,
-                    const int32_t* tree_slot_idx, const int32_t* parent, void* stream) {
+int vamla_split_partials(const vamla_params* p, const uint16_t* q, const uint16_t* kv_pool,
+                         const int32_t* prefix_slot_idx, const int32_t* tree_slot_idx, const int32_t* parent,
+                         void* stream) {
   vamla_plan_info pl;
   int st = prologue(p, &pl);
   if (st != VAMLA_OK) return st;
   if (!q || !kv_pool || !tree_slot_idx || !parent) return VAMLA_ERR_INVALID_ARG;
-  return tail_launch(p, pl, q, kv_pool, tree_slot_idx, parent, (hipStream_t)stream);
+  if (p->total_prefix > 0 && !prefix_slot_idx) return VAMLA_ERR_INVALID_ARG;
+  return split_launch(p, pl, q, kv_pool, prefix_slot_idx, tree_slot_idx, parent, (hipStream_t)stream);
 }
 
 int vamla_lse_merge(const vamla_params* p, uint16_t* out, float* lse, void* stream) {

@@ -70,16 +70,20 @@ def test_plan_covers_the_problem(L, k):
     assert info.grid_items % 8 == 0 and info.grid_items >= p.batch * info.row_tiles * info.max_chunks
     items = p.batch * info.row_tiles * info.max_chunks
     assert info.off_part_lse >= info.off_part_o + items * 128 * 64 * 16
-    assert info.off_tail_o >= info.off_part_lse + items * 64 * 4
+    assert info.workspace_bytes >= info.off_part_lse + items * 64 * 4
     assert info.workspace_bytes == vb.workspace_size(p)
-    for off in (info.off_part_o, info.off_part_lse, info.off_tail_o, info.off_tail_lse):
+    for off in (info.off_part_o, info.off_part_lse):
         assert off % 256 == 0
 
 
 def test_plan_fills_the_chip_for_the_64k_config(L):
-    info = vb.plan(prob(3))
+    p = prob(3)
+    info = vb.plan(p)
     items = info.row_tiles * info.max_chunks
     assert 200 <= items <= 256        # one round of work items over 256 CUs
+    # the last chunk also streams the tree's two key tiles; it must not be the longest item
+    last = p.max_prefix - (info.max_chunks - 1) * info.chunk
+    assert math.ceil(last / 64) * 64 + 128 <= info.chunk
 
 
 def test_explicit_chunk_is_kept(L):

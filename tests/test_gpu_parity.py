@@ -139,55 +139,42 @@ def test_determinism():
 
 # --- stage-level parity ----------------------------------------------------
 
-def test_stage_prefix_partials():
+@pytest.mark.parametrize("lens,chunk", [([700, 250, 0], 256), ([128, 64, 0], 64)])
+def test_stage_split_partials(lens, chunk):
+    # chunk partials on their own: every chunk but a request's last covers its
+    # prefix keys only; the last one (chunk 0 with no prefix) also the tree keys
+    # under the ancestor mask, which is the oracle's prefix and tree partials merged
     import torch
     rng = np.random.default_rng(8)
-    x = small([700, 250], [gen.random_tree(9, rng), gen.random_tree(4, rng)], 8, seed=20)
-    p = problem(x, chunk=256)
+    parents = [gen.random_tree(9, rng), gen.bounded_tree(33, rng), gen.random_tree(65, rng)]
+    x = small(lens, parents, 8, seed=20)
+    p = problem(x, chunk=chunk)
     d = to_dev(x)
     ws = vb.Workspace(p)
-    vb.prefix_partials(p, d["q"], d["kv_pool"], d["prefix_slot_idx"], d["cu_prefix"], d["cu_tree"], ws)
+    log(f"[case] split partials lens={lens} chunk={chunk}")
+    vb.split_partials(p, d["q"], d["kv_pool"], d["prefix_slot_idx"], d["tree_slot_idx"], d["parent"],
+                      d["cu_prefix"], d["cu_tree"], ws)
     torch.cuda.synchronize()
     v = vb.workspace_views(p, ws)
     part_o = v["part_o"].cpu().numpy()
     part_lse = v["part_lse"].cpu().numpy()
     for b in range(x.batch):
         L, N, H = x.prefix_len(b), x.tree_len(b), x.num_heads
-        for s in range((L + 255) // 256):
-            ro, rl = vo.prefix_partial(x.q, x.pool, x.prefix_slot_idx, x.cu_prefix, x.cu_tree, b,
-                                       s * 256, min(L, (s + 1) * 256), x.scale)
-            ro = ro.reshape(N * H, 512)
-            rl = rl.reshape(N * H)
+        S = max(1, -(-L // chunk))
+        for s in range(S):
+            parts = []
+            if L:
+                parts.append(vo.prefix_partial(x.q, x.pool, x.prefix_slot_idx, x.cu_prefix, x.cu_tree, b,
+                                               s * chunk, min(L, (s + 1) * chunk), x.scale))
+            if s == S - 1:
+                parts.append(vo.tree_partial(x.q, x.pool, x.tree_slot_idx, x.parent, x.cu_tree, b, x.scale))
+            ro, rl = vo.merge_partials([(o.reshape(N * H, 512), l.reshape(N * H)) for o, l in parts])
             rows = np.arange(N * H)
             tile, rit = rows // 64, rows % 64
             got_l = part_lse[b, tile, s, rit]
             got_o = part_o[b, tile, s].reshape(len(rows), 128, 64, 4)[np.arange(len(rows)), :, rit, :].reshape(len(rows), 512)
             assert_close_lse(got_l, rl, f"partial b={b} s={s}")
             np.testing.assert_allclose(got_o, ro, atol=2e-3 * np.abs(ro).max() + 1e-6)
-
-
-def test_stage_tree_tail():
-    import torch
-    rng = np.random.default_rng(9)
-    parents = [gen.random_tree(12, rng), gen.bounded_tree(33, rng), np.array([-1], np.int32)]
-    x = small([10, 20, 30], parents, 6, seed=21)
-    p = problem(x)
-    d = to_dev(x)
-    ws = vb.Workspace(p)
-    vb.tree_tail(p, d["q"], d["kv_pool"], d["tree_slot_idx"], d["parent"], d["cu_prefix"], d["cu_tree"], ws)
-    torch.cuda.synchronize()
-    v = vb.workspace_views(p, ws)
-    tail_o = v["tail_o"].cpu().numpy()
-    tail_l = v["tail_lse"].cpu().numpy()
-    for b in range(x.batch):
-        N, H = x.tree_len(b), x.num_heads
-        ro, rl = vo.tree_partial(x.q, x.pool, x.tree_slot_idx, x.parent, x.cu_tree, b, x.scale)
-        rows = np.arange(N * H)
-        tile, rit = rows // 64, rows % 64
-        got_l = tail_l[b, tile, rit]
-        got_o = np.stack([tail_o[b, tile[i], :, rit[i], :].reshape(512) for i in rows])
-        np.testing.assert_allclose(got_l, rl.reshape(-1), atol=1e-4)
-        np.testing.assert_allclose(got_o, ro.reshape(N * H, 512), atol=1e-4)
 
 
 def test_slot_gather_bit_exact():
