@@ -10,71 +10,81 @@
 // Phase 2; "The Architecture Detective: ...", "The Message in Full").
 // Chunks past a request's prefix were never written and are not read.
 //
-// Layout: partials are [item][128 d4][64 rows][4 floats], so thread = row reads
-// coalesced 16-byte pieces; grid = (request x row tile) x column groups.
+// Layout: partials are [item][128 d4][64 rows][4 floats].  A 256-thread
+// workgroup covers one row tile and four float4 column groups; thread =
+// (column group, row), so each wave reads one coalesced 1 KB piece per chunk.
+// Every thread keeps its chunks' loads in flight at once: the pass is a
+// stream over the partials and needs many waves per CU to reach HBM speed.
 
 #include "kernels.h"
 
 namespace vamla {
 namespace {
 
-constexpr int kD4PerBlock = 4;   // float4 column groups per thread
+constexpr int kGroups = 4;          // float4 column groups per workgroup
+constexpr int kMaxMergeUnroll = 16; // chunks whose loads are issued together
 
-__global__ __launch_bounds__(kRowTile) void lse_merge_kernel(MergeArgs a) {
+__global__ __launch_bounds__(kRowTile * kGroups) void lse_merge_kernel(MergeArgs a) {
   const int item = blockIdx.x;
   const int b = item / a.row_tiles;
   const int tile = item - b * a.row_tiles;
   const int t0 = a.cu_tree[b];
   const int rows_b = (a.cu_tree[b + 1] - t0) * a.num_heads;
-  const int rit = threadIdx.x;
+  const int rit = threadIdx.x & (kRowTile - 1);
+  const int d4 = blockIdx.y * kGroups + (threadIdx.x >> 6);
   const int r = tile * kRowTile + rit;
   if (r >= rows_b) return;
   const int L = a.cu_prefix[b + 1] - a.cu_prefix[b];
   // a prefix longer than max_prefix is a caller error; never read past the plan
   const int S = max(1, min((L + a.chunk - 1) / a.chunk, a.max_chunks));
 
-  const size_t tb = (size_t)b * a.row_tiles + tile;
-  const size_t p0 = tb * a.max_chunks;
+  const size_t p0 = ((size_t)b * a.row_tiles + tile) * a.max_chunks;
+  const float* lse_p = a.part_lse + p0 * kRowTile + rit;
+  const float4* o_p = (const float4*)a.part_o + (p0 * kD4 + d4) * kRowTile + rit;
+  const size_t o_stride = (size_t)kD4 * kRowTile;          // float4s per chunk partial
+
   float m = -INFINITY;
-  for (int s = 0; s < S; ++s) m = fmaxf(m, a.part_lse[(p0 + s) * kRowTile + rit]);
+  for (int s = 0; s < S; ++s) m = fmaxf(m, lse_p[s * kRowTile]);
   float sum = 0.f;
-  for (int s = 0; s < S; ++s) sum += __expf(a.part_lse[(p0 + s) * kRowTile + rit] - m);
-  const float lse = m + logf(sum);
-
-  const size_t orow = (size_t)t0 * a.num_heads + r;   // global row (t, h)
-  if (blockIdx.y == 0) a.lse[orow] = lse;
-
-  const int d4_0 = blockIdx.y * kD4PerBlock;
-  float4 acc[kD4PerBlock];
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int s0 = 0; s0 < S; s0 += kMaxMergeUnroll) {
+    float4 v[kMaxMergeUnroll];
+    float w[kMaxMergeUnroll];
 #pragma unroll
-  for (int j = 0; j < kD4PerBlock; ++j) acc[j] = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int s = 0; s < S; ++s) {
-    const float ws = __expf(a.part_lse[(p0 + s) * kRowTile + rit] - lse);
+    for (int j = 0; j < kMaxMergeUnroll; ++j) {
+      if (s0 + j < S) {
+        v[j] = o_p[(size_t)(s0 + j) * o_stride];
+        w[j] = lse_p[(s0 + j) * kRowTile];
+      }
+    }
 #pragma unroll
-    for (int j = 0; j < kD4PerBlock; ++j) {
-      const float4 v = *(const float4*)(a.part_o + (((p0 + s) * kD4 + d4_0 + j) * kRowTile + rit) * 4);
-      acc[j].x = fmaf(ws, v.x, acc[j].x);
-      acc[j].y = fmaf(ws, v.y, acc[j].y);
-      acc[j].z = fmaf(ws, v.z, acc[j].z);
-      acc[j].w = fmaf(ws, v.w, acc[j].w);
+    for (int j = 0; j < kMaxMergeUnroll; ++j) {
+      if (s0 + j < S) {
+        const float e = __expf(w[j] - m);
+        sum += e;
+        acc.x = fmaf(e, v[j].x, acc.x);
+        acc.y = fmaf(e, v[j].y, acc.y);
+        acc.z = fmaf(e, v[j].z, acc.z);
+        acc.w = fmaf(e, v[j].w, acc.w);
+      }
     }
   }
+  const float inv = 1.f / sum;
+  const size_t orow = (size_t)t0 * a.num_heads + r;   // global row (t, h)
+  if (d4 == 0) a.lse[orow] = m + logf(sum);
   // bf16, round to nearest even
-  uint16_t* o = a.out + orow * kDv + d4_0 * 4;
-#pragma unroll
-  for (int j = 0; j < kD4PerBlock; ++j) {
-    const __bf16 h0 = (__bf16)acc[j].x, h1 = (__bf16)acc[j].y, h2 = (__bf16)acc[j].z, h3 = (__bf16)acc[j].w;
-    uint2 pk;
-    pk.x = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
-    pk.y = (uint32_t)__builtin_bit_cast(uint16_t, h2) | ((uint32_t)__builtin_bit_cast(uint16_t, h3) << 16);
-    *(uint2*)(o + j * 4) = pk;
-  }
+  const __bf16 h0 = (__bf16)(acc.x * inv), h1 = (__bf16)(acc.y * inv), h2 = (__bf16)(acc.z * inv),
+               h3 = (__bf16)(acc.w * inv);
+  uint2 pk;
+  pk.x = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
+  pk.y = (uint32_t)__builtin_bit_cast(uint16_t, h2) | ((uint32_t)__builtin_bit_cast(uint16_t, h3) << 16);
+  *(uint2*)(a.out + orow * kDv + d4 * 4) = pk;
 }
 
 }  // namespace
 
 hipError_t launch_lse_merge(const MergeArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL(lse_merge_kernel, dim3(a.batch * a.row_tiles, kD4 / kD4PerBlock), dim3(kRowTile), 0,
+  hipLaunchKernelGGL(lse_merge_kernel, dim3(a.batch * a.row_tiles, kD4 / kGroups), dim3(kRowTile * kGroups), 0,
                      stream, a);
   return hipGetLastError();
 }
