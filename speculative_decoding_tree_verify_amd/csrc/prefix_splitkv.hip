@@ -76,10 +76,13 @@ constexpr int kPrePV = 4;           // same for PV (two transposed reads each)
 constexpr int kQkSteps = kDqk / 16; // 36 MFMA steps over the query columns
 
 // Which gather instruction of the next tile (0..17, or -1 for none) rides
-// along with MFMA step g of a tile (QK steps 0..35, then PV steps 36..67).
-// Issuing them spread out keeps the wave from stalling on a full address
-// queue.
-__device__ __forceinline__ constexpr int dma_at(int g) { return (g < 36 && (g & 1) == 0) ? (g >> 1) : -1; }
+// along with MFMA step g of a tile (QK steps 0..35, then PV steps 36..67; the
+// PV loop offers steps 36 + 8ks + 4 + c, ks, c in 0..3).  The two rope
+// instructions go first, the 16 latent ones with the PV steps, where the MFMA
+// pipe rather than the LDS limits the wave.
+__device__ __forceinline__ constexpr int dma_at(int g) {
+  return g < 2 ? 16 + g : ((g >= 40 && ((g - 40) & 4) == 0) ? ((g - 40) >> 3) * 4 + ((g - 40) & 3) : -1);
+}
 // Buffer descriptor word 3 for plain dword loads (32-bit data format, no swizzle)
 constexpr int kRsrcWord3 = 0x00020000;
 
@@ -211,17 +214,20 @@ __device__ __forceinline__ float sum_xor32(float x) {
   return p + q;
 }
 
-// P = exp2(s*scale - m) in bf16 for this lane's 16 raw scores; lsum += sum P.
+// P = exp2(s*scale - m) in bf16 for this lane's 16 raw scores; lsum += sum P
+// (four partial sums, so the adds do not form one long dependency chain).
 __device__ __forceinline__ void pack_p(const f32x16& v, float scale, float m, bf16x8 (&pb)[2], float& lsum) {
+  float part[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const float p = __builtin_amdgcn_exp2f(fmaf(v[half * 8 + e], scale, -m));
-      lsum += p;
+      part[e & 3] += p;
       pb[half][e] = (__bf16)p;
     }
   }
+  lsum += (part[0] + part[1]) + (part[2] + part[3]);
 }
 
 // One staged 64-key tile for this wave.  `first` (workgroup-uniform): the
@@ -232,9 +238,9 @@ __device__ __forceinline__ bool tile_math(const uint8_t* lds, Xchg& x, const bf1
                                           uint64_t vis, float scale_log2,
                                           const Lane& ln, const uint16_t* pool, const TileSlots& ng_sl,
                                           uint8_t* ng_lds) {
-  // S^T of this wave's key block over all 576 columns; even and odd steps
-  // accumulate separately so consecutive MFMAs never depend on each other
-  f32x16 sp0 = {}, sp1 = {};
+  // S^T of this wave's key block over all 576 columns (a chain of dependent
+  // MFMAs on one accumulator issues at full rate)
+  f32x16 v = {};
   {
     bf16x8 kf[kPreQK];
 #pragma unroll
@@ -243,14 +249,12 @@ __device__ __forceinline__ bool tile_math(const uint8_t* lds, Xchg& x, const bf1
     for (int i = 0; i < kQkSteps; ++i) {
       const bf16x8 cur = kf[i % kPreQK];
       if (i + kPreQK < kQkSteps) kf[i % kPreQK] = kfrag(lds, ln, i + kPreQK);
-      if (i & 1) sp1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur, qf[i], sp1, 0, 0, 0);
-      else sp0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur, qf[i], sp0, 0, 0, 0);
+      v = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur, qf[i], v, 0, 0, 0);
       // on a chunk's last tile the gather refetches valid rows into the idle buffer
       if (dma_at(i) >= 0) gather_one(pool, ng_sl, ng_lds, ln.w, ln.lane, dma_at(i));
       __builtin_amdgcn_sched_barrier(0);
     }
   }
-  f32x16 v = sp0 + sp1;
   // lane holds keys 32*hf + 8*(r/4) + 4*hl + r%4 of row l32 (raw scores)
   if (nvalid < kKeyTile) {
 #pragma unroll
