@@ -36,6 +36,18 @@ from speculative_decoding_tree_verify_amd import inputs as gen  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
+
+# HBM bytes per launch of the split kernel on the default workload, from two
+# rocprofv3 --pmc passes (FETCH_SIZE, WRITE_SIZE; summary under profiles/),
+# each scaled by what the counter reads for a plain device copy of known size
+# (FETCH_SIZE reports half of the bytes a copy reads, WRITE_SIZE all it
+# writes).  Valid only for the kernel sources they were taken on: keyed by
+# their sha256, and reported as null for any other build.
+MEASURED_TRAFFIC = {
+    # sha256(prefix_splitkv.hip + kernels.h): (fetch KiB, write KiB, fetch scale, write scale)
+    "d41e503abf6949f57c01e6bd07dc5f22c5da77b01997000210cda055ec693568": (59352.6, 31260.9, 2.0, 1.0),
+}
+KERNEL_SOURCES = ("prefix_splitkv.hip", "kernels.h")
 KV_ROW_BYTES = 576 * 2
 FLOPS_PER_ROW_KEY = 2 * (576 + 512)
 POOL_ROTATION_BYTES = 768 << 20   # > 3x the Infinity Cache
@@ -65,6 +77,19 @@ def algorithmic(x: gen.VerifyInputs):
     io_bytes = T * H * (KV_ROW_BYTES + 512 * 2 + 4)
     return dict(kv_bytes=kv_rows * KV_ROW_BYTES, prefix_flops=prefix_flops, tail_flops=tail_flops,
                 io_bytes=io_bytes)
+
+
+def split_kernel_traffic():
+    import hashlib
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "speculative_decoding_tree_verify_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    m = MEASURED_TRAFFIC.get(h.hexdigest())
+    if m is None:
+        return None
+    fetch_kib, write_kib, fs, ws = m
+    return int(round((fetch_kib * fs + write_kib * ws) * 1024))
 
 
 def time_events(fn, iters: int) -> float:
@@ -233,7 +258,8 @@ def main():
             "peak": MFMA_BF16_PEAK_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
-            "traffic": None,
+            "traffic": split_kernel_traffic(),
+            "traffic_unit": "bytes per launch",
         },
         "cpu_baseline": ({k: v for k, v in cpu.items() if k != "ms_per_step"} if cpu else None),
     }
