@@ -11,10 +11,9 @@ namespace vamla {
 constexpr int kDqk = 576;                  // latent 512 + rope 64
 constexpr int kDv = 512;
 constexpr int kChunks16 = kDqk / 8;        // 72 sixteen-byte pieces per pool row
-constexpr int kKeyTile = 64;               // keys per LDS tile
-constexpr int kRowTile = 64;               // query rows per prefix work item (2 wave pairs x 32)
+constexpr int kKeyTile = 64;               // chunk sizes are multiples of this
+constexpr int kRowTile = 64;               // query rows per split work item
 constexpr int kD4 = kDv / 4;               // 128 float4 groups per output row
-constexpr int kTileBytes = kChunks16 * kKeyTile * 16;   // 73728 B of LDS per key tile
 constexpr int kMaxTree = 65;
 constexpr int kMaxHeads = 128;
 

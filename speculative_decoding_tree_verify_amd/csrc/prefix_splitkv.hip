@@ -1,4 +1,4 @@
-// Prefix split-KV attention for DDTree verify over an MLA latent pool (gfx950).
+// Split-KV pass of DDTree verify attention over an MLA latent pool (gfx950).
 //
 // Every tree node attends densely to the whole prefix with no mask ("The
 // Architecture Detective: Uncovering FlashMLA's Potential for Blackwell DDTree
@@ -6,55 +6,49 @@
 // latent head of width 576 whose first 512 columns are V).  The prefix is cut
 // into fixed chunks of logical positions; each chunk yields a normalised
 // partial (o_s, lse_s) that a later pass merges by log-sum-exp ("The Anatomy of
-// a Kernel Investigation", "The Reasoning Process: A Deep Dive", Phase 2).
+// a Kernel Investigation", "The Reasoning Process: A Deep Dive", Phase 2).  The
+// last chunk of a request also takes the request's tree keys, each row seeing
+// only its node's ancestors and itself ("Mapping the Optimization Landscape
+// for DDTree Verify Attention", "Input Knowledge Required to Understand This
+// Message", item 1), so one partial covers both.
 //
-// Work item = (request b, row tile of 64 query rows, chunk s); one 256-thread
-// workgroup (4 waves) per item.  All H*N query rows of a request read every
-// prefix key, so the pass is a dense contraction and runs on MFMA
-// (v_mfma_f32_32x32x16_bf16, fp32 accumulation).
+// Work item = (request b, row tile of 64 query rows, chunk s); one 512-thread
+// workgroup per item, two waves per SIMD, specialised:
+//   * 4 QK waves.  Wave w holds all 576 query columns of 32 rows (rows
+//     32(w>>1) ..) in VGPRs and, per 32-key tile, computes the scores of its 16
+//     keys (keys 16(w&1) ..): S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (A = K
+//     from LDS, B = Q; each K fragment feeds both 16-row halves).  It then
+//     forms P = exp2(S*scale*log2e - m) in bf16 and stores it to LDS in the PV
+//     waves' operand layout.
+//   * 4 PV waves.  Wave c accumulates O^T += V^T P^T for output columns
+//     [128c, 128c+128) of all 64 rows with v_mfma_f32_32x32x16_bf16 (A = V^T
+//     read by ds_read_b64_tr_b16, B = P; each V^T fragment feeds both row
+//     halves), 128 accumulator VGPRs, and issues the gather of the tiles ahead.
+// The SIMD's matrix core is shared by its QK and PV wave, so one wave's
+// softmax, LDS waits and gather issue overlap the other's MFMAs.  One barrier
+// per tile: QK waves score tile t and publish P(t) while PV waves consume
+// P(t-1) and fill the ring slot of tile t+2.
 //
-// Waves form two pairs; pair p owns query rows [32p, 32p+32) of the tile and
-// wave (p, h) of the pair key block h (keys [32h, 32h+32) of each tile) and
-// output columns [256h, 256h+256):
-//   * QK: holds all 576 query columns of the pair's rows in VGPRs and computes
-//     the scores S^T = K Q^T of its key block (A = K from LDS, B = Q).  In the
-//     32x32 accumulator layout each lane owns one query row.
-//   * softmax: P = exp2(S*scale*log2e - m) in bf16 for those 32 keys, also
-//     stored to LDS for the partner (it is the partner's MFMA operand too).
-//   * PV: O^T += V^T P^T for its 256 output columns over all 64 keys (A = V^T
-//     read from the same LDS tile by ds_read_b64_tr_b16, B = P): first over
-//     its own key block, then, after the tile's one barrier, over the
-//     partner's with the P the partner stored.
-// Per wave: Q 144 VGPRs and a 32x256 fp32 accumulator (128 AGPRs).  Splitting
-// the pair by keys rather than by query columns leaves no partial scores to
-// exchange, so a tile needs one barrier besides the one that hands over the
-// staged tile.
-//
-// Gather: buffer_load_dwordx4 ... lds moves 16 bytes per lane straight into
-// LDS (no VGPR staging).  Latent rows use the buffer (MUBUF) form with one
-// descriptor per row, rope rows the global form issued through asm (see
-// dma16_global): the compiler counts a global LDS-DMA as a pending LDS access
-// until it completes, which would turn every LDS operand wait of the tile
-// into a full drain; a buffer DMA is tracked as a plain vector-memory op.  Per key, one instruction fetches the 1 KB latent part of
-// its pool row (8 cache lines); one instruction fetches the 128-byte rope parts
-// of 8 keys.  Slots are held one per lane and loaded two tiles ahead.  LDS tile
-// layout (72 KB per 64 keys):
+// Gather: LDS-DMA moves 16 bytes per lane straight into LDS.  Latent rows: one
+// 64-lane buffer_load_dwordx4 ... lds per key with a per-row descriptor; rope
+// rows: one 64-lane global_load_lds_dwordx4 per 8 keys with 64-bit per-lane
+// addresses (buffer offsets are 32-bit, rows may lie past 4 GiB).  Both are
+// issued as asm: the compiler would otherwise make every LDS read wait for
+// them (it cannot tell the ring slots apart); the waits are explicit vmcnt
+// counts before each barrier.  A 4-slot ring of 36 KB tiles (32 keys):
 //   latent: key k at k*1024, 16-byte piece c at slot c ^ g(k),
 //           g(k) = ((k & 3) << 2) | ((k >> 2) & 3)
-//   rope:   key k at 64 KB + k*128, piece c at slot c ^ ((k >> 1) & 7)
-// Lane-linear DMA writes pick the piece each lane loads, so the swizzle is
-// free; it keeps the ds_read_b128 (QK, 16 lanes per LDS cycle) and
-// ds_read_b64_tr_b16 (PV, 32 lanes per cycle) patterns free of bank
-// conflicts.  Tiles are double-buffered: the 18 gather instructions of tile
-// t+1 are spread over the QK loop of tile t.
+//   rope:   key k at 32 KB + k*128, piece c at slot c ^ ((k >> 1) & 7)
+// keeps the QK ds_read_b128 pattern (16 lanes per LDS cycle) and the PV
+// ds_read_b64_tr_b16 pattern (32 lanes per cycle) free of bank conflicts.
 //
 // Softmax reference: each row keeps a reference m (log2 units) instead of a
-// running max, so the accumulator is never rescaled and stays in AGPRs.  The
-// first tile sets m to the pair's tile max.  While every score stays within
-// kSlack of m, exp2(s - m) <= 2^kSlack, far inside bf16/fp32 range.  A tile
-// that breaks this (rare) makes the whole workgroup restart its chunk with
-// m raised to that tile's max plus kSlack of headroom; m only grows, by more
-// than kSlack per restart, so restarts are few and the result is the same.
+// running max, so the accumulators are never rescaled.  The first tile sets m
+// to the row's max over that tile.  While every score stays within kSlack of
+// m, exp2(s - m) <= 2^kSlack, far inside bf16/fp32 range.  A tile that breaks
+// this (rare) makes the workgroup restart its item with m raised to that
+// tile's max plus kSlack; each restart needs a new, larger tile max, so there
+// are at most as many restarts as tiles.
 
 #include "kernels.h"
 
@@ -64,50 +58,31 @@ namespace {
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(4))) short i16x4;
 typedef __attribute__((ext_vector_type(8))) short i16x8;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 constexpr float kLn2 = 0.69314718055994530942f;
-constexpr float kSlack = 16.0f;     // scores may exceed the reference by this much (log2 units)
-constexpr int kRopeBase = 64 * 1024;
-constexpr int kPreQK = 4;           // LDS operand reads in flight ahead of their MFMA (QK)
-constexpr int kPrePV = 4;           // same for PV (two transposed reads each)
-constexpr int kQkSteps = kDqk / 16; // 36 MFMA steps over the query columns
-
-// Which gather instruction of the next tile (0..17, or -1 for none) rides
-// along with MFMA step g of a tile (QK steps 0..35, then PV steps 36..67; the
-// PV loop offers steps 36 + 8ks + 4 + c, ks, c in 0..3).  The two rope
-// instructions go first, the 16 latent ones with the PV steps, where the MFMA
-// pipe rather than the LDS limits the wave.
-__device__ __forceinline__ constexpr int dma_at(int g) {
-  return g < 2 ? 16 + g : ((g >= 40 && ((g - 40) & 4) == 0) ? ((g - 40) >> 3) * 4 + ((g - 40) & 3) : -1);
-}
-// Buffer descriptor word 3 for plain dword loads (32-bit data format, no swizzle)
+constexpr float kSlack = 16.0f;
+constexpr int kKT = 32;                       // keys per tile
+constexpr int kTileLds = kKT * kDqk * 2;      // 36864 B
+constexpr int kRopeOff = kKT * 1024;          // rope parts after the 32 latent rows
+constexpr int kRing = 4;                      // tiles staged in LDS
+constexpr int kQSteps = kDqk / 32;            // 18 steps of v_mfma_f32_16x16x32_bf16
+constexpr int kPreQK = 4;
 constexpr int kRsrcWord3 = 0x00020000;
-
-// Exchange area, 48 bytes per lane and wave: wave w stores the P operand of
-// its key block in v[w][0..1] and its row max and restart vote in v[w][2].
-struct __attribute__((aligned(16))) Xchg {
-  float4 v[4][3][64];               // [wave][16-byte part][lane], 12 KB
-};
+constexpr int kMaxTreeTiles = (kMaxTree + kKT - 1) / kKT;   // 3
 
 __device__ __forceinline__ int swz_latent(int k) { return ((k & 3) << 2) | ((k >> 2) & 3); }
 __device__ __forceinline__ int swz_rope(int k) { return (k >> 1) & 7; }
 
-// Workgroup barrier that waits only for this wave's LDS operations.  A fence
-// would also wait for the in-flight gathers (LDS DMA counts as LDS stores),
-// which must keep running under the math.
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-// base ^ c, computed where it is used (an opaque xor keeps the compiler from
-// hoisting every variant of a swizzled base into its own register)
 __device__ __forceinline__ int xor_at_use(int base, int c) {
   if (c == 0) return base;
   int r;
-  asm volatile("v_xor_b32 %0, %2, %1" : "=v"(r) : "v"(base), "i"(c));   // literal must be src0
+  asm volatile("v_xor_b32 %0, %2, %1" : "=v"(r) : "v"(base), "i"(c));
   return r;
 }
 
@@ -118,13 +93,6 @@ __device__ __forceinline__ bf16x8 tr_pair(const uint8_t* base, int off1, int off
   return __builtin_bit_cast(bf16x8, v);
 }
 
-// LDS DMA of 16 bytes per lane from a 64-bit per-lane address into LDS at
-// lds_addr + 16*lane (the rope parts of 8 keys from 8 unrelated rows; buffer
-// offsets are 32-bit, so rows past 4 GiB of the pool need this form).  Written
-// as asm so that the compiler's wait tracking does not see it: it would count
-// the op as a pending LDS access until it completes and drain every LDS wait
-// behind it.  The data is read only after the s_waitcnt 0 and barrier that
-// start the next tile.  M0 carries the LDS address and is restored.
 __device__ __forceinline__ void dma16_global(const void* src, uint32_t lds_addr) {
   uint32_t saved;
   asm volatile(
@@ -138,234 +106,112 @@ __device__ __forceinline__ void dma16_global(const void* src, uint32_t lds_addr)
       : "memory");
 }
 
-// Pool slots of one wave's 16 keys of a tile, one per lane: `lat` holds the
-// slot of key 16w + (lane & 15), rope[j] that of key 16w + 8j + (lane >> 3).
-struct TileSlots {
-  uint32_t lat, rope[2];
-};
-
-// Gather instruction d (0..17) of this wave's share of one key tile, keys
-// [16w, 16w+16): d < 16 moves the 1 KB latent part of key 16w+d (one 64-lane
-// instruction, 8 cache lines; the slot is read out of lane d), d = 16, 17 the
-// 128-byte rope parts of keys 16w + 8(d-16) + (lane >> 3) (8 keys per 64-lane
-// instruction).  Lanes write 16 bytes each, lane-linearly, and load the piece
-// the swizzle puts there.
-__device__ __forceinline__ void gather_one(const uint16_t* pool, const TileSlots& sl, uint8_t* lds, int w, int lane,
-                                           int d) {
-  if (d < 16) {
-    const uint32_t slot = __builtin_amdgcn_readlane(sl.lat, d);
-    const __amdgpu_buffer_rsrc_t row = __builtin_amdgcn_make_buffer_rsrc((void*)(pool + (size_t)slot * kDqk), 0, 1024,
-                                                                         kRsrcWord3);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(row, (lds_void*)(lds + (16 * w + d) * 1024), 16,
-                                             (uint32_t)xor_at_use(lane << 4, swz_latent(d) << 4), 0, 0, 0);
-  } else {
-    const int j = d - 16;
-    const int kl = 8 * j + (lane >> 3);                      // key within the wave's 16
-    const uint8_t* src = (const uint8_t*)(pool + (size_t)sl.rope[j] * kDqk + 512) + (((lane & 7) ^ swz_rope(kl)) << 4);
-    dma16_global(src, (uint32_t)(uintptr_t)(lds_void*)(lds + kRopeBase + (16 * w + 8 * j) * 128));
-  }
+// Buffer LDS-DMA of 16 bytes per lane (row descriptor, per-lane offset) into
+// LDS at lds_addr + 16*lane, issued as asm like dma16_global: the compiler
+// neither waits for it nor treats later LDS reads as possibly aliasing it.
+__device__ __forceinline__ void dma16_buffer(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, uint32_t lds_addr) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %1, %2, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(rsrc), "s"(lds_addr)
+      : "memory");
 }
 
-__device__ __forceinline__ void gather_tile(const uint16_t* pool, const TileSlots& sl, uint8_t* lds, int w,
-                                            int lane) {
-#pragma unroll
-  for (int d = 0; d < 18; ++d) gather_one(pool, sl, lds, w, lane, d);
+// A 4-byte global load issued as asm: its result is valid only after an
+// explicit vmcnt wait that names the register.
+__device__ __forceinline__ uint32_t load_u32_async(const int* p) {
+  uint32_t v;
+  asm volatile("global_load_dword %0, %1, off" : "=v"(v) : "v"(p) : "memory");
+  return v;
 }
 
-struct Lane {
-  int w, pr, hf, hl, l32, lane;
-  // Swizzled LDS addresses are written base ^ (step-dependent bits) + immediate:
-  // key = 32*hf + l32 (the lane's key of the wave's block)
-  int qk_lat;        // latent: key*1024 | ((hl ^ g(key)) << 4); step s: ^ 32*(s&7), + 256*(s>>3)
-  int qk_rope;       // rope: 64K + key*128 | ((hl ^ h(key)) << 4); rope step r: ^ 32*r
-  int pv[2];         // PV transposed reads, key group sec: column block c: ^ 64*c
-};
-
-struct RowState {
-  float m;   // reference max of scaled scores (log2 units), shared by the pair
-  float l;   // this lane's share of the row sum
-};
-
-// K fragment of QK step s (0..35) of this wave's key block: 16-byte pieces
-// 2s and 2s+1 of the 576 columns (latent for s < 32, then rope); lane half
-// hl takes piece 2s + hl.
-__device__ __forceinline__ bf16x8 kfrag(const uint8_t* lds, const Lane& ln, int s) {
-  if (s < 32) return *(const bf16x8*)(lds + xor_at_use(ln.qk_lat, 32 * (s & 7)) + (s >> 3) * 256);
-  return *(const bf16x8*)(lds + xor_at_use(ln.qk_rope, 32 * (s - 32)));
+// max without the NaN-quieting the compiler adds around fmaxf (scores are
+// never signalling NaNs here; -inf marks masked keys)
+__device__ __forceinline__ float vmax(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
 }
 
-// x[lane] and x[lane ^ 32] for every lane, through one v_permlane32_swap of
-// two copies of x (afterwards each lane holds one of the two values in each
-// register).  Written as asm: handed the same value twice, the builtin's two
-// results get folded into one.
-__device__ __forceinline__ void halves32(float x, float& p, float& q) {
-  p = x;
-  q = x;
+__device__ __forceinline__ void swap32(float& p, float& q) {
   asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(p), "+v"(q));
 }
-__device__ __forceinline__ float max_xor32(float x) {
-  float p, q;
-  halves32(x, p, q);
-  return fmaxf(p, q);
+__device__ __forceinline__ void swap16(float& p, float& q) {
+  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(p), "+v"(q));
+}
+// max / sum of x over the four lanes l % 16 == const
+__device__ __forceinline__ float max4(float x) {
+  float p = x, q = x;
+  swap16(p, q);
+  float y = vmax(p, q);
+  p = y;
+  q = y;
+  swap32(p, q);
+  return vmax(p, q);
+}
+__device__ __forceinline__ float sum4(float x) {
+  float p = x, q = x;
+  swap16(p, q);
+  float y = p + q;
+  p = y;
+  q = y;
+  swap32(p, q);
+  return p + q;
 }
 __device__ __forceinline__ float sum_xor32(float x) {
-  float p, q;
-  halves32(x, p, q);
+  float p = x, q = x;
+  swap32(p, q);
   return p + q;
 }
 
-// P = exp2(s*scale - m) in bf16 for this lane's 16 raw scores; lsum += sum P
-// (four partial sums, so the adds do not form one long dependency chain).
-__device__ __forceinline__ void pack_p(const f32x16& v, float scale, float m, bf16x8 (&pb)[2], float& lsum) {
-  float part[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int half = 0; half < 2; ++half) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float p = __builtin_amdgcn_exp2f(fmaf(v[half * 8 + e], scale, -m));
-      part[e & 3] += p;
-      pb[half][e] = (__bf16)p;
-    }
+// Gather instruction d (0..8) of PV wave c for one 32-key tile: d < 8 moves
+// the 1 KB latent part of key 8c+d (slot read out of lane 8d of sv), d = 8 the
+// 128-byte rope parts of keys 8c .. 8c+7 (lane l: key 8c + (l >> 3)).
+__device__ __forceinline__ void gather_one(const uint16_t* pool, uint32_t sv, uint8_t* buf, int c, int lane, int d) {
+  if (d < 8) {
+    const uint32_t slot = __builtin_amdgcn_readlane(sv, 8 * d);
+    const int key = 8 * c + d;
+    const __amdgpu_buffer_rsrc_t row = __builtin_amdgcn_make_buffer_rsrc((void*)(pool + (size_t)slot * kDqk), 0, 1024,
+                                                                         kRsrcWord3);
+    dma16_buffer(row, (uint32_t)((lane ^ swz_latent(key)) << 4), (uint32_t)(uintptr_t)(lds_void*)(buf + key * 1024));
+  } else {
+    const int kl = 8 * c + (lane >> 3);
+    const uint8_t* src = (const uint8_t*)(pool + (size_t)sv * kDqk + 512) + (((lane & 7) ^ swz_rope(kl)) << 4);
+    dma16_global(src, (uint32_t)(uintptr_t)(lds_void*)(buf + kRopeOff + 8 * c * 128));
   }
-  lsum += (part[0] + part[1]) + (part[2] + part[3]);
 }
 
-// One staged 64-key tile for this wave.  `first` (workgroup-uniform): the
-// chunk's reference m is not set yet.  Returns true when the workgroup must
-// restart its chunk; the tile's contribution is then discarded.
-__device__ __forceinline__ bool tile_math(const uint8_t* lds, Xchg& x, const bf16x8 (&qf)[kQkSteps],
-                                          f32x16 (&o)[8], RowState& st, bool first, int nvalid, bool masked,
-                                          uint64_t vis, float scale_log2,
-                                          const Lane& ln, const uint16_t* pool, const TileSlots& ng_sl,
-                                          uint8_t* ng_lds) {
-  // S^T of this wave's key block over all 576 columns (a chain of dependent
-  // MFMAs on one accumulator issues at full rate)
-  f32x16 v = {};
-  {
-    bf16x8 kf[kPreQK];
-#pragma unroll
-    for (int i = 0; i < kPreQK; ++i) kf[i] = kfrag(lds, ln, i);
-#pragma unroll
-    for (int i = 0; i < kQkSteps; ++i) {
-      const bf16x8 cur = kf[i % kPreQK];
-      if (i + kPreQK < kQkSteps) kf[i % kPreQK] = kfrag(lds, ln, i + kPreQK);
-      v = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur, qf[i], v, 0, 0, 0);
-      // on a chunk's last tile the gather refetches valid rows into the idle buffer
-      if (dma_at(i) >= 0) gather_one(pool, ng_sl, ng_lds, ln.w, ln.lane, dma_at(i));
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  }
-  // lane holds keys 32*hf + 8*(r/4) + 4*hl + r%4 of row l32 (raw scores)
-  if (nvalid < kKeyTile) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r)
-      if (32 * ln.hf + 8 * (r >> 2) + 4 * ln.hl + (r & 3) >= nvalid) v[r] = -INFINITY;
-  }
-  if (masked) {       // tree keys: bit k of vis = key k of the tile is visible to this row
-#pragma unroll
-    for (int r = 0; r < 16; ++r)
-      if (((vis >> (32 * ln.hf + 8 * (r >> 2) + 4 * ln.hl + (r & 3))) & 1) == 0) v[r] = -INFINITY;
-  }
-  float mt = v[0];
-#pragma unroll
-  for (int r = 1; r < 16; ++r) mt = fmaxf(mt, v[r]);
-  mt = max_xor32(mt) * scale_log2;                 // row max over the block's 32 keys, log2 units
-  if (first) {
-    // the reference is the pair's max over this tile
-    x.v[ln.w][2][ln.lane] = make_float4(mt, 0.f, 0.f, 0.f);
-    lds_barrier();
-    st.m = fmaxf(mt, x.v[ln.w ^ 1][2][ln.lane].x);
-  }
-  bf16x8 pb[2];
-  float lsum = 0.f;
-  pack_p(v, scale_log2, st.m, pb, lsum);
-  const float want = __any(mt > st.m + kSlack) ? 1.f : 0.f;   // never on the first tile
-  x.v[ln.w][0][ln.lane] = __builtin_bit_cast(float4, pb[0]);
-  x.v[ln.w][1][ln.lane] = __builtin_bit_cast(float4, pb[1]);
-  x.v[ln.w][2][ln.lane] = make_float4(mt, want, 0.f, 0.f);
-  // O^T += V^T P^T for this wave's 128 output columns [128w, 128w+128) over
-  // all 64 rows and all 64 keys.  P of the four (row block, key block) pairs
-  // comes from the four waves: this wave's from registers, the rest from LDS
-  // behind the tile's barrier.  Each V^T fragment (32 columns x 16 keys) feeds
-  // the MFMAs of both row blocks.  P keeps the key order of the score
-  // accumulator layout and the transposed V reads take the keys in that same
-  // order.  Key steps ks = 2*kb' + h run over the own key block (kb' = 0)
-  // first; o[4*rb' + c] accumulates column block c of row block rb' (rb' = 0:
-  // this pair's rows).
-  {
-    const int own0 = ln.pv[0] + ln.hf * 32768, own1 = ln.pv[1] + ln.hf * 32768;
-    const int oth0 = own0 ^ 32768, oth1 = own1 ^ 32768;
-    auto vfrag = [&](int ks, int c) {
-      const int off = (ks & 1) * 16 * 1024;
-      const int b0 = ks < 2 ? own0 : oth0, b1 = ks < 2 ? own1 : oth1;
-      return tr_pair(lds, xor_at_use(b0, 64 * c) + off, xor_at_use(b1, 64 * c) + off);
-    };
-    bf16x8 vf[4];
-#pragma unroll
-    for (int c = 0; c < 4; ++c) vf[c] = vfrag(0, c);
-    lds_barrier();
-    // P operands of the other waves, read as the key steps reach them:
-    // (this pair's rows, other key block) from w^1, (other rows, own block)
-    // from w^2, (other rows, other block) from w^3
-    auto pfrom = [&](int wv, int h) { return __builtin_bit_cast(bf16x8, x.v[wv][h][ln.lane]); };
-    bf16x8 q0n = pb[0], q1n = pfrom(ln.w ^ 2, 0);
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const bf16x8 q0 = q0n;                           // this pair's rows
-      const bf16x8 q1 = q1n;                           // the other pair's rows
-      if (ks < 3) {
-        const int n = ks + 1, h = n & 1;
-        q0n = n < 2 ? pb[h] : pfrom(ln.w ^ 1, h);
-        q1n = pfrom(n < 2 ? ln.w ^ 2 : ln.w ^ 3, h);
-      }
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        o[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[c], q0, o[c], 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        o[4 + c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[c], q1, o[4 + c], 0, 0, 0);
-        if (ks < 3) vf[c] = vfrag(ks + 1, c);
-        if (dma_at(36 + 8 * ks + 4 + c) >= 0) gather_one(pool, ng_sl, ng_lds, ln.w, ln.lane, dma_at(36 + 8 * ks + 4 + c));
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
-  }
-  // The restart vote is read only now: a restarting chunk discards this
-  // tile's accumulation anyway.  Every wave stored its wave-uniform vote in
-  // all lanes, so each lane reads its own.
-  const float any_flag = x.v[0][2][ln.lane].y + x.v[1][2][ln.lane].y + x.v[2][2][ln.lane].y + x.v[3][2][ln.lane].y;
-  if (__builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, any_flag)) != 0) {
-    // a score ran past the reference: restart the chunk with headroom
-    const float mp = fmaxf(mt, x.v[ln.w ^ 1][2][ln.lane].x);
-    st.m = fmaxf(st.m, mp) + kSlack;
-    st.l = 0.f;
-#pragma unroll
-    for (int d = 0; d < 8; ++d) o[d] = f32x16{};
-    return true;
-  }
-  st.l += lsum;
-  return false;
-}
+struct Shared {
+  uint8_t pbuf[2][4][1024];                   // P operands, [parity][ks*2 + rb][lane*16]
+  float mt[4][64];                            // QK waves: row max of the tile (first tile and restarts)
+  float want[2][4];                           // QK waves: restart vote per tile parity
+  float rowl[64];                             // final row sums (QK -> PV)
+  float rowm[64];                             // final row references
+  uint32_t vis[kRowTile][4];                  // tree masks: bit k of word tt = tree key 32tt + k visible
+  int par[kMaxTree];
+};
 
-__global__ __launch_bounds__(256, 1) void prefix_splitkv_kernel(PrefixArgs a) {
-  __shared__ __attribute__((aligned(1024))) uint8_t lds0[kTileBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t lds1[kTileBytes];
-  __shared__ Xchg x;
-  __shared__ int par_s[kMaxTree];                 // the request's parent array
-  __shared__ uint64_t vis_s[kRowTile][2];         // per row: visible tree keys 0..63, 64..127
+__global__ __launch_bounds__(512, 1) void prefix_splitkv_kernel(PrefixArgs a) {
+  // Four staged tiles as separate arrays: the PV loop names each one
+  // statically, so the compiler can tell a gather's destination from the
+  // tile being read and does not drain the gathers before every LDS read.
+  __shared__ __attribute__((aligned(1024))) uint8_t tile0[kTileLds];
+  __shared__ __attribute__((aligned(1024))) uint8_t tile1[kTileLds];
+  __shared__ __attribute__((aligned(1024))) uint8_t tile2[kTileLds];
+  __shared__ __attribute__((aligned(1024))) uint8_t tile3[kTileLds];
+  __shared__ __attribute__((aligned(16))) Shared sh;
+  auto ring = [&](int i) -> uint8_t* { i &= 3; return i == 0 ? tile0 : i == 1 ? tile1 : i == 2 ? tile2 : tile3; };
 
-  Lane ln;
-  ln.lane = threadIdx.x & 63;
-  ln.w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  ln.pr = ln.w >> 1;
-  ln.hf = ln.w & 1;
-  ln.hl = ln.lane >> 5;
-  ln.l32 = ln.lane & 31;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const bool is_qk = w < 4;
 
-  // Work item; consecutive logical items (the row tiles of one chunk) land on
-  // one XCD, since workgroup i is dispatched to XCD i % 8.
+  // work item (same decomposition as the 4-wave kernel)
   const int per_xcd = a.grid_items >> 3;
   const int k = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
   const int tiles_chunks = a.row_tiles * a.max_chunks;
@@ -376,7 +222,6 @@ __global__ __launch_bounds__(256, 1) void prefix_splitkv_kernel(PrefixArgs a) {
   const int tile = rem - s * a.row_tiles;
   const int p0 = a.cu_prefix[b];
   const int L = a.cu_prefix[b + 1] - p0;
-  // chunks of this request; with no prefix, chunk 0 still carries the tree
   const int nchunks = max(1, min((L + a.chunk - 1) / a.chunk, a.max_chunks));
   if (s >= nchunks) return;
   const int kbeg = s * a.chunk;
@@ -385,165 +230,291 @@ __global__ __launch_bounds__(256, 1) void prefix_splitkv_kernel(PrefixArgs a) {
   const int n_b = a.cu_tree[b + 1] - t0;
   const int rows_b = n_b * a.num_heads;
   if (tile * kRowTile >= rows_b) return;
-  // The request's last chunk also takes its tree keys (<= 65, so at most two
-  // tiles) under the ancestor-or-self mask ("Mapping the Optimization
-  // Landscape for DDTree Verify Attention", "Input Knowledge Required to
-  // Understand This Message", item 1): one partial then covers both.
-  const int ntp = kend > kbeg ? (kend - kbeg + kKeyTile - 1) / kKeyTile : 0;   // prefix tiles
-  const int ntt = s == nchunks - 1 ? (min(n_b, kMaxTree) + kKeyTile - 1) / kKeyTile : 0;   // tree tiles
-
-  const int row_in_tile = ln.pr * 32 + ln.l32;
-  const int row = tile * kRowTile + row_in_tile;
-  const bool row_ok = row < rows_b;
-
-  // the pair's query rows, all 576 columns: lane (l32, hl) holds 16-byte
-  // piece 2s + hl of its row for step s (latent pieces 0..63, rope 64..71)
-  bf16x8 qf[kQkSteps];
-  {
-    const uint16_t* qrow = a.q + ((size_t)t0 * a.num_heads + (row_ok ? row : 0)) * kDqk;
-#pragma unroll
-    for (int s2 = 0; s2 < kQkSteps; ++s2) {
-      const int piece = 2 * s2 + ln.hl;
-      bf16x8 v = *(const bf16x8*)(qrow + piece * 8);
-      qf[s2] = row_ok ? v : bf16x8{};
-    }
-  }
-
-  f32x16 o[8];
-#pragma unroll
-  for (int d = 0; d < 8; ++d) o[d] = f32x16{};
-  RowState st{-INFINITY, 0.f};
-
-  // lane constants for LDS reads (layout in the header comment)
-  {
-    const int key = 32 * ln.hf + ln.l32;
-    ln.qk_lat = (key * 1024) | ((ln.hl ^ swz_latent(key)) << 4);
-    ln.qk_rope = (kRopeBase + key * 128) | ((ln.hl ^ swz_rope(key)) << 4);
-    // PV: lane (block gb, sub-lane sl) reads keys kb*32 + h*16 + 4*hl + (sl >> 2) (+8*sec),
-    // columns 128w + 32c + 16*(gb & 1) + 4*(sl & 3) .. +3 for column block c
-    const int gb = ln.lane >> 4, sl = ln.lane & 15;
-    const int kk = 4 * ln.hl + (sl >> 2);
-    const int cp = 2 * (gb & 1) + ((sl >> 1) & 1);
-#pragma unroll
-    for (int sec = 0; sec < 2; ++sec) {
-      const int gk = ((sl >> 2) << 2) | (ln.hl + 2 * sec);   // g(key) of key kk + 8*sec
-      ln.pv[sec] = ((kk + 8 * sec) * 1024 + 256 * ln.w + 8 * (sl & 1)) | ((cp ^ gk) << 4);
-    }
-  }
-
-  // Slots of this wave's keys of tile t, one vector load per lane (see
-  // TileSlots); keys past the end of the chunk take the last key's slot (a
-  // valid index; masked in the math).
+  const int n_tree = min(n_b, kMaxTree);
+  const int ntp = kend > kbeg ? (kend - kbeg + kKT - 1) / kKT : 0;
+  const int ntt = s == nchunks - 1 ? (n_tree + kKT - 1) / kKT : 0;
   const int ntiles = ntp + ntt;
-  auto load_slots = [&](int t) {
-    // prefix tiles first, then tree tiles; keys past the end of either list
-    // take its last slot; a tile index past the last tile re-reads it
-    t = min(t, ntiles - 1);
-    const bool tree = t >= ntp;
-    const int* list = tree ? a.tree_slot + t0 : a.prefix_slot + p0;
-    const int base = (tree ? (t - ntp) * kKeyTile : kbeg + t * kKeyTile) + 16 * ln.w;
-    const int last = tree ? min(n_b, kMaxTree) - 1 : kend - 1;
-    TileSlots r;
-    r.lat = (uint32_t)list[min(base + (ln.lane & 15), last)];
-    r.rope[0] = (uint32_t)list[min(base + (ln.lane >> 3), last)];
-    r.rope[1] = (uint32_t)list[min(base + 8 + (ln.lane >> 3), last)];
-    return r;
-  };
 
   if (ntt > 0) {
-    // Ancestor-or-self sets of this tile's rows as bit masks over the tree
-    // keys.  A parent that does not precede its child ends a walk, so a
-    // malformed array cannot loop; rows past the request's nodes see the root.
-    for (int i = threadIdx.x; i < min(n_b, kMaxTree); i += blockDim.x) par_s[i] = a.parent[t0 + i];
+    for (int i = threadIdx.x; i < n_tree; i += blockDim.x) sh.par[i] = a.parent[t0 + i];
     __syncthreads();
     if (threadIdx.x < kRowTile) {
       const int r = tile * kRowTile + (int)threadIdx.x;
-      int j = r < rows_b ? min(r / a.num_heads, min(n_b, kMaxTree) - 1) : 0;
-      uint64_t m0 = 0, m1 = 0;
+      int j = r < rows_b ? min(r / a.num_heads, n_tree - 1) : 0;
+      uint32_t m[4] = {0u, 0u, 0u, 0u};
       for (int step = 0; step < kMaxTree && j >= 0; ++step) {
-        if (j < 64) m0 |= 1ull << j; else m1 |= 1ull << (j - 64);
-        const int p = par_s[j];
+        m[j >> 5] |= 1u << (j & 31);
+        const int p = sh.par[j];
         j = (p < j) ? p : -1;
       }
-      vis_s[threadIdx.x][0] = m0;
-      vis_s[threadIdx.x][1] = m1;
+      for (int i = 0; i < 4; ++i) sh.vis[threadIdx.x][i] = m[i];
     }
-    // made visible by the barrier that starts the first tile
   }
 
-  TileSlots sl_next;
-  // put tile 0 into `buf` (item start and restarts)
-  auto prime = [&](uint8_t* buf) {
-    gather_tile(a.pool, load_slots(0), buf, ln.w, ln.lane);
-    sl_next = load_slots(1);
+  // The two roles run separate code (separate register sets) in lockstep:
+  // both execute the same sequence of barriers.
+  //   QK wave w (0..3): pair pr = w >> 1 (rows 32pr..32pr+31), key half
+  //     hf = w & 1 (keys 16hf..16hf+15 of each tile).
+  //   PV wave c = w - 4 (0..3): output columns [128c, 128c+128), all 64 rows.
+  const size_t pidx = ((size_t)b * a.row_tiles + tile) * a.max_chunks + s;
+  if (is_qk) {
+    const int pr = w >> 1, hf = w & 1, q4 = lane >> 4, l16 = lane & 15;
+    bf16x8 qf[kQSteps][2];
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      const int row = tile * kRowTile + 32 * pr + 16 * nb + l16;
+      const bool ok = row < rows_b;
+      const uint16_t* qrow = a.q + ((size_t)t0 * a.num_heads + (ok ? row : 0)) * kDqk;
+#pragma unroll
+      for (int st = 0; st < kQSteps; ++st) {
+        const bf16x8 v = *(const bf16x8*)(qrow + (4 * st + q4) * 8);
+        qf[st][nb] = ok ? v : bf16x8{};
+      }
+    }
+    const int key = 16 * hf + l16;
+    const int qk_lat = (key * 1024) | ((q4 ^ swz_latent(key)) << 4);
+    const int qk_rope = (kRopeOff + key * 128) | ((q4 ^ swz_rope(key)) << 4);
+    float m_ref[2] = {-INFINITY, -INFINITY};   // rows 16nb + l16 of the pair
+    float lsum[2] = {0.f, 0.f};
+    bool have_ref = false;
+    for (;;) {                                 // again after a restart
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();                         // prologue: tiles 0, 1 staged
+      bool restart = false;
+      for (int it = 0; it <= ntiles; ++it) {
+        if (it < ntiles) {
+          const uint8_t* buf = ring(it);
+          f32x4 sacc[2] = {f32x4{}, f32x4{}};
+          auto kfrag = [&](int st) {
+            if (st < 16) return *(const bf16x8*)(buf + xor_at_use(qk_lat, 64 * (st & 3)) + 256 * (st >> 2));
+            return *(const bf16x8*)(buf + xor_at_use(qk_rope, 64 * (st - 16)));
+          };
+          bf16x8 kf[kPreQK];
+#pragma unroll
+          for (int i = 0; i < kPreQK; ++i) kf[i] = kfrag(i);
+#pragma unroll
+          for (int st = 0; st < kQSteps; ++st) {
+            const bf16x8 cur = kf[st % kPreQK];
+            if (st + kPreQK < kQSteps) kf[st % kPreQK] = kfrag(st + kPreQK);
+            sacc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur, qf[st][0], sacc[0], 0, 0, 0);
+            sacc[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur, qf[st][1], sacc[1], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+          // lane holds keys 16hf + 4q4 + r (r = 0..3) of rows 32pr + 16nb + l16
+          const bool tree = it >= ntp;
+          const int nvalid = tree ? kKT : min(kKT, kend - kbeg - it * kKT);
+#pragma unroll
+          for (int nb = 0; nb < 2; ++nb) {
+            if (nvalid < kKT) {
+#pragma unroll
+              for (int r = 0; r < 4; ++r)
+                if (16 * hf + 4 * q4 + r >= nvalid) sacc[nb][r] = -INFINITY;
+            }
+            if (tree) {
+              const uint32_t vm = sh.vis[32 * pr + 16 * nb + l16][it - ntp];
+#pragma unroll
+              for (int r = 0; r < 4; ++r)
+                if (((vm >> (16 * hf + 4 * q4 + r)) & 1u) == 0) sacc[nb][r] = -INFINITY;
+            }
+          }
+          float mt[2];
+#pragma unroll
+          for (int nb = 0; nb < 2; ++nb)
+            mt[nb] = max4(vmax(vmax(sacc[nb][0], sacc[nb][1]), vmax(sacc[nb][2], sacc[nb][3]))) * a.scale_log2;
+          // the row max of this wave's 16 keys now sits in all four lanes of
+          // the row; lanes 0..31 store it for row j = lane (nb = lane >> 4)
+          sh.mt[w][lane] = q4 == 0 ? mt[0] : mt[1];
+          if (it == 0 && !have_ref) {
+            lds_barrier();
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb) m_ref[nb] = fmaxf(mt[nb], sh.mt[w ^ 1][16 * nb + l16]);
+          }
+          // P in bf16, stored in the PV B-operand layout: block (ks = hf,
+          // rb = pr), lane L = j + 32*(q4 >> 1) holds keys 8*(q4 >> 1) .. +7 of
+          // row j; this lane's 4 keys are bytes 8*(q4 & 1) .. +7 of it
+          uint8_t* pbl = sh.pbuf[it & 1][2 * hf + pr];
+          bool want = false;
+#pragma unroll
+          for (int nb = 0; nb < 2; ++nb) {
+            float ps[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) ps[r] = __builtin_amdgcn_exp2f(fmaf(sacc[nb][r], a.scale_log2, -m_ref[nb]));
+            lsum[nb] += (ps[0] + ps[1]) + (ps[2] + ps[3]);
+            typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
+            bf16x4 pk;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) pk[r] = (__bf16)ps[r];
+            const int j = 16 * nb + l16;
+            *(bf16x4*)(pbl + (j + 32 * (q4 >> 1)) * 16 + 8 * (q4 & 1)) = pk;
+            want |= mt[nb] > m_ref[nb] + kSlack;
+          }
+          const float wv = __any(want) ? 1.f : 0.f;
+          if (lane == 0) sh.want[it & 1][w] = wv;
+        }
+        lds_barrier();
+        if (it < ntiles && sh.want[it & 1][0] + sh.want[it & 1][1] + sh.want[it & 1][2] + sh.want[it & 1][3] != 0.f) {
+          restart = true;
+          break;
+        }
+      }
+      if (!restart) break;
+      // restart with the pair's max over the offending tile plus headroom
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        m_ref[nb] = fmaxf(m_ref[nb], fmaxf(sh.mt[w][16 * nb + l16], sh.mt[w ^ 1][16 * nb + l16])) + kSlack;
+        lsum[nb] = 0.f;
+      }
+      have_ref = true;
+      __syncthreads();
+    }
+    // row sums: the four lanes of the row, then the partner wave
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) lsum[nb] = sum4(lsum[nb]);
+    sh.mt[w][lane] = q4 == 0 ? lsum[0] : lsum[1];
+    lds_barrier();
+    if (hf == 0 && q4 < 2) {
+      const int j = 32 * pr + lane;
+      const float l = sh.mt[w][lane] + sh.mt[w ^ 1][lane];
+      sh.rowl[j] = l;
+      if (tile * kRowTile + j < rows_b) a.part_lse[pidx * kRowTile + j] = m_ref[q4] * kLn2 + logf(l);
+    }
+    lds_barrier();
+    return;
+  }
+
+  // ---------------- PV waves ----------------
+  const int c = w - 4;
+  f32x16 o[8];
+#pragma unroll
+  for (int d = 0; d < 8; ++d) o[d] = f32x16{};
+  // transposed V reads: lane (block bb = lane/16, e = (lane/4)%4, s2 = lane%4)
+  int pvb[2];
+  {
+    const int bb = lane >> 4, e = (lane >> 2) & 3, s2 = lane & 3;
+#pragma unroll
+    for (int hi = 0; hi < 2; ++hi) {
+      const int key = 8 * (bb >> 1) + e + 4 * hi;
+      pvb[hi] = (key * 1024 + 256 * c + 8 * (s2 & 1)) | (((2 * (bb & 1) + (s2 >> 1)) ^ swz_latent(key)) << 4);
+    }
+  }
+  // slot of key 8c + (lane >> 3) of tile t; valid after the next vmcnt wait
+  auto load_slot = [&](int t) -> uint32_t {
+    t = min(t, ntiles - 1);
+    const bool tree = t >= ntp;
+    const int* list = tree ? a.tree_slot + t0 : a.prefix_slot + p0;
+    const int base = tree ? (t - ntp) * kKT : kbeg + t * kKT;
+    const int last = tree ? n_tree - 1 : kend - 1;
+    return load_u32_async(list + min(base + 8 * c + (lane >> 3), last));
   };
-  prime(lds0);
-  int t = 0;                 // tile held by the buffer processed next
-  bool restart = false;      // workgroup-uniform
-  bool have_ref = false;     // workgroup-uniform: the reference m is set
-  // one tile: `cur` holds tile t while `nxt` receives tile t+1
-  auto half_step = [&](uint8_t* cur, uint8_t* nxt) -> bool {
+  bool have_ref = false;
+  for (;;) {
+    // Slot ring: svd holds the slots of tile it+2 (gathered in iteration it),
+    // svn those of tile it+3.  Each iteration loads the next slots before its
+    // gathers, so the in-order vector-memory counter never makes a slot load
+    // wait for a gather.
+    uint32_t svd, svn;
+    {
+      uint32_t s0 = load_slot(0), s1 = load_slot(1);
+      svd = load_slot(2);
+      svn = load_slot(3);
+      asm volatile("s_waitcnt vmcnt(0)" : "+v"(s0), "+v"(s1), "+v"(svd), "+v"(svn) :: "memory");
+#pragma unroll
+      for (int d = 0; d < 9; ++d) gather_one(a.pool, s0, tile0, c, lane, d);
+      if (ntiles > 1) {
+#pragma unroll
+        for (int d = 0; d < 9; ++d) gather_one(a.pool, s1, tile1, c, lane, d);
+      }
+    }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (restart) {
-      restart = false;                 // tile_math has cleared o and l
-      t = 0;
-      prime(cur);
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
-    } else if (t >= ntiles) {
-      return false;
+    constexpr int kPrePV = 3;
+    auto vfrag_of = [&](const uint8_t* rbuf, int f) {
+      const int ks = f >> 2, cb = f & 3;
+      return tr_pair(rbuf, xor_at_use(pvb[0], 64 * cb) + ks * 16384, xor_at_use(pvb[1], 64 * cb) + ks * 16384);
+    };
+    bool restart = false;
+    for (int it = 0; it <= ntiles; ++it) {
+      if (it == 0 && !have_ref) lds_barrier();   // the QK waves' first-tile max exchange
+      const bool do_dma = it + 2 < ntiles;
+      uint8_t* dbuf = ring(it + 2);
+      uint32_t svf = load_slot(it + 4);           // issued before this iteration's gathers
+      if (it >= 1) {
+        // PV of tile it-1, the gather of tile it+2 riding along
+        const uint8_t* rbuf = ring(it - 1);
+        const uint8_t* pbp = sh.pbuf[(it - 1) & 1][0];
+        bf16x8 pop[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pop[i] = *(const bf16x8*)(pbp + i * 1024 + lane * 16);
+        // fragment f = 4ks + cb: V^T of columns block cb over key step ks,
+        // read kPrePV fragments ahead of its two MFMAs (one per row block)
+        auto vfrag = [&](int f) { return vfrag_of(rbuf, f); };
+        bf16x8 vf[kPrePV];
+#pragma unroll
+        for (int f = 0; f < kPrePV; ++f) vf[f] = vfrag(f);
+#pragma unroll
+        for (int f = 0; f < 8; ++f) {
+          const int ks = f >> 2, cb = f & 3;
+          const bf16x8 av = vf[f % kPrePV];
+          if (f + kPrePV < 8) vf[f % kPrePV] = vfrag(f + kPrePV);
+#pragma unroll
+          for (int rb = 0; rb < 2; ++rb) {
+            o[cb + 4 * rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pop[2 * ks + rb], o[cb + 4 * rb], 0, 0, 0);
+            const int g = 2 * f + rb;
+            if (do_dma && (g & 1) == 0) gather_one(a.pool, svd, dbuf, c, lane, g >> 1);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+        if (do_dma) gather_one(a.pool, svd, dbuf, c, lane, 8);
+      } else if (do_dma) {
+#pragma unroll
+        for (int d = 0; d < 9; ++d) gather_one(a.pool, svd, dbuf, c, lane, d);
+      }
+      // the gather of tile it+1 (issued one iteration ago) and the slot load
+      // above must have landed; this iteration's nine gathers may stay in
+      // flight (vector memory completes in order)
+      if (do_dma) asm volatile("s_waitcnt vmcnt(9)" : "+v"(svf) :: "memory");
+      else asm volatile("s_waitcnt vmcnt(0)" : "+v"(svf) :: "memory");
+      svd = svn;
+      svn = svf;
+      lds_barrier();
+      if (it < ntiles && sh.want[it & 1][0] + sh.want[it & 1][1] + sh.want[it & 1][2] + sh.want[it & 1][3] != 0.f) {
+        restart = true;
+        break;
+      }
     }
-    const bool tree = t >= ntp;
-    const int nvalid = tree ? kKeyTile : min(kKeyTile, kend - kbeg - t * kKeyTile);
-    const uint64_t vis = tree ? vis_s[row_in_tile][t - ntp] : ~0ull;
-    restart = tile_math(cur, x, qf, o, st, !have_ref, nvalid, tree, vis, a.scale_log2, ln, a.pool, sl_next, nxt);
+    if (!restart) break;
+    __builtin_amdgcn_s_waitcnt(0);
+#pragma unroll
+    for (int d = 0; d < 8; ++d) o[d] = f32x16{};
     have_ref = true;
-    // slots of tile t+2; their latency hides under the wait for tile t+1
-    sl_next = load_slots(t + 2);
-    ++t;
-    return true;
-  };
-  for (;;) {
-    if (!half_step(lds0, lds1)) break;
-    if (!half_step(lds1, lds0)) break;
+    __syncthreads();
   }
-
-  // Row sums and references of both row blocks: this wave holds l over its
-  // key block for this pair's rows; the partner holds the other key block,
-  // the other pair the other rows.
-  const float lpair = sum_xor32(st.l);
-  lds_barrier();                      // everyone is done reading the last P operands
-  x.v[ln.w][0][ln.lane] = make_float4(lpair, st.m, 0.f, 0.f);
+  lds_barrier();                                  // QK waves publish row sums
   lds_barrier();
-  const float4 e1 = x.v[ln.w ^ 1][0][ln.lane], e2 = x.v[ln.w ^ 2][0][ln.lane], e3 = x.v[ln.w ^ 3][0][ln.lane];
-  const float l_rb[2] = {lpair + e1.x, e2.x + e3.x};
-  const size_t pidx = ((size_t)b * a.row_tiles + tile) * a.max_chunks + s;
   float* po = a.part_o + pidx * (kD4 * kRowTile * 4);
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb) {
-    const int rit = 32 * (ln.pr ^ rb) + ln.l32;
+    const int rit = 32 * rb + (lane & 31);
     if (tile * kRowTile + rit >= rows_b) continue;
-    const float inv = 1.0f / l_rb[rb];
+    const float inv = __builtin_amdgcn_rcpf(sh.rowl[rit]);   // <= 1 ulp
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
+    for (int cb = 0; cb < 4; ++cb) {
 #pragma unroll
       for (int rq = 0; rq < 4; ++rq) {
-        const int d4 = (4 * ln.w + c) * 8 + 2 * rq + ln.hl;
-        const f32x16& acc = o[4 * rb + c];
+        const int d4 = (4 * c + cb) * 8 + 2 * rq + (lane >> 5);
+        const f32x16& acc = o[cb + 4 * rb];
         const float4 v = make_float4(acc[4 * rq] * inv, acc[4 * rq + 1] * inv, acc[4 * rq + 2] * inv,
                                      acc[4 * rq + 3] * inv);
         *(float4*)(po + ((size_t)d4 * kRowTile + rit) * 4) = v;
       }
     }
   }
-  if (row_ok && ln.hf == 0 && ln.hl == 0) a.part_lse[pidx * kRowTile + row_in_tile] = st.m * kLn2 + logf(l_rb[0]);
 }
 
 }  // namespace
 
 hipError_t launch_prefix_splitkv(const PrefixArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL(prefix_splitkv_kernel, dim3(a.grid_items), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(prefix_splitkv_kernel, dim3(a.grid_items), dim3(512), 0, stream, a);
   return hipGetLastError();
 }
 
