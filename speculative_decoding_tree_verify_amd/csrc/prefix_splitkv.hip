@@ -26,8 +26,12 @@
 //     halves), 128 accumulator VGPRs, and issues the gather of the tiles ahead.
 // The SIMD's matrix core is shared by its QK and PV wave, so one wave's
 // softmax, LDS waits and gather issue overlap the other's MFMAs.  One barrier
-// per tile: QK waves score tile t and publish P(t) while PV waves consume
-// P(t-1) and fill the ring slot of tile t+2.
+// per tile and a three-stage pipeline: in iteration t the QK waves score tile
+// t and turn the scores of tile t-1 into P(t-1) (that softmax runs while tile
+// t's first K fragments are in flight); the PV waves multiply V(t-2), read
+// into VGPRs during iteration t-1, by P(t-2), read V(t-1) fragment by
+// fragment as the registers free up, and gather tile t+2.  The restart vote
+// of tile t-2 is read early and tested just before the barrier.
 //
 // Gather: LDS-DMA moves 16 bytes per lane straight into LDS.  Latent rows: one
 // 64-lane buffer_load_dwordx4 ... lds per key with a per-row descriptor; rope
@@ -35,7 +39,9 @@
 // addresses (buffer offsets are 32-bit, rows may lie past 4 GiB).  Both are
 // issued as asm: the compiler would otherwise make every LDS read wait for
 // them (it cannot tell the ring slots apart); the waits are explicit vmcnt
-// counts before each barrier.  A 4-slot ring of 36 KB tiles (32 keys):
+// counts before each barrier.  The PV waves' LDS reads are asm too, with
+// lgkmcnt waits counted by hand, so that the V reads of the next tile stay in
+// flight under the current tile's MFMAs.  A 4-slot ring of 36 KB tiles (32 keys):
 //   latent: key k at k*1024, 16-byte piece c at slot c ^ g(k),
 //           g(k) = ((k & 3) << 2) | ((k >> 2) & 3)
 //   rope:   key k at 32 KB + k*128, piece c at slot c ^ ((k >> 1) & 7)
@@ -44,7 +50,8 @@
 //
 // Softmax reference: each row keeps a reference m (log2 units) instead of a
 // running max, so the accumulators are never rescaled.  The first tile sets m
-// to the row's max over that tile.  While every score stays within kSlack of
+// to the row's max over that tile (the two QK waves of a row pair exchange
+// their halves through LDS at the first barrier).  While every score stays within kSlack of
 // m, exp2(s - m) <= 2^kSlack, far inside bf16/fp32 range.  A tile that breaks
 // this (rare) makes the workgroup restart its item with m raised to that
 // tile's max plus kSlack; each restart needs a new, larger tile max, so there
@@ -70,7 +77,7 @@ constexpr int kTileLds = kKT * kDqk * 2;      // 36864 B
 constexpr int kRopeOff = kKT * 1024;          // rope parts after the 32 latent rows
 constexpr int kRing = 4;                      // tiles staged in LDS
 constexpr int kQSteps = kDqk / 32;            // 18 steps of v_mfma_f32_16x16x32_bf16
-constexpr int kPreQK = 4;
+constexpr int kPreQK = 4;                     // K fragments read ahead
 constexpr int kRsrcWord3 = 0x00020000;
 constexpr int kMaxTreeTiles = (kMaxTree + kKT - 1) / kKT;   // 3
 
@@ -130,6 +137,44 @@ __device__ __forceinline__ uint32_t load_u32_async(const int* p) {
   return v;
 }
 
+
+// LDS reads issued as asm: the compiler does not count them, so each use is
+// preceded by an explicit lgkmcnt wait that names the register.  LDS
+// operations of one wave complete in order, so lgkmcnt(n) means "all but the
+// last n issued LDS operations have landed".
+#define VAMLA_LGKM_CASE(N) case N: asm volatile("s_waitcnt lgkmcnt(" #N ")" : "+v"(r) :: "memory"); break;
+template <typename T>
+__device__ __forceinline__ void wait_lgkm(int n, T& r) {
+  switch (n) {
+    VAMLA_LGKM_CASE(0) VAMLA_LGKM_CASE(1) VAMLA_LGKM_CASE(2) VAMLA_LGKM_CASE(3) VAMLA_LGKM_CASE(4)
+    VAMLA_LGKM_CASE(5) VAMLA_LGKM_CASE(6) VAMLA_LGKM_CASE(7) VAMLA_LGKM_CASE(8) VAMLA_LGKM_CASE(9)
+    VAMLA_LGKM_CASE(10) VAMLA_LGKM_CASE(11) VAMLA_LGKM_CASE(12) VAMLA_LGKM_CASE(13) VAMLA_LGKM_CASE(14)
+    default: asm volatile("s_waitcnt lgkmcnt(15)" : "+v"(r) :: "memory"); break;
+  }
+}
+#undef VAMLA_LGKM_CASE
+#define VAMLA_B128_CASE(O) case O: asm volatile("ds_read_b128 %0, %1 offset:" #O : "=v"(v) : "v"(addr)); break;
+__device__ __forceinline__ bf16x8 ds_b128(uint32_t addr, int off) {
+  bf16x8 v;
+  switch (off) {
+    VAMLA_B128_CASE(0) VAMLA_B128_CASE(1024) VAMLA_B128_CASE(2048) VAMLA_B128_CASE(3072)
+    default: __builtin_trap();
+  }
+  return v;
+}
+#undef VAMLA_B128_CASE
+#define VAMLA_TR_CASE(O) case O: asm volatile("ds_read_b64_tr_b16 %0, %1 offset:" #O : "=v"(v) : "v"(addr)); break;
+__device__ __forceinline__ i16x4 ds_tr(uint32_t addr, int off) {
+  i16x4 v;
+  switch (off) {
+    VAMLA_TR_CASE(0) VAMLA_TR_CASE(16384)
+    default: __builtin_trap();
+  }
+  return v;
+}
+#undef VAMLA_TR_CASE
+__device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)(lds_void*)p; }
+
 // max without the NaN-quieting the compiler adds around fmaxf (scores are
 // never signalling NaNs here; -inf marks masked keys)
 __device__ __forceinline__ float vmax(float a, float b) {
@@ -188,7 +233,7 @@ __device__ __forceinline__ void gather_one(const uint16_t* pool, uint32_t sv, ui
 
 struct Shared {
   uint8_t pbuf[2][4][1024];                   // P operands, [parity][ks*2 + rb][lane*16]
-  float mt[4][64];                            // QK waves: row max of the tile (first tile and restarts)
+  float mt[3][4][64];                         // QK waves: row max of the tile, by tile index mod 3
   float want[2][4];                           // QK waves: restart vote per tile parity
   float rowl[64];                             // final row sums (QK -> PV)
   float rowm[64];                             // final row references
@@ -277,21 +322,64 @@ __global__ __launch_bounds__(512, 1) void prefix_splitkv_kernel(PrefixArgs a) {
     float m_ref[2] = {-INFINITY, -INFINITY};   // rows 16nb + l16 of the pair
     float lsum[2] = {0.f, 0.f};
     bool have_ref = false;
+    int restart_tile = 0;
     for (;;) {                                 // again after a restart
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();                         // prologue: tiles 0, 1 staged
       bool restart = false;
-      for (int it = 0; it <= ntiles; ++it) {
+      // Iteration it scores tile it and turns the scores of tile it-1 into
+      // P; the PV waves consume P(it-2).  The softmax runs while this
+      // tile's first K fragments are in flight.
+      f32x4 sprev[2] = {f32x4{}, f32x4{}};   // masked scores of tile it-1
+      int mi = 0;                            // it mod 3
+      float mprev[2] = {0.f, 0.f};           // their row max (log2 units), this wave's keys
+      for (int it = 0; it <= ntiles + 1; ++it) {
+        const uint8_t* buf = ring(it);
+        auto kfrag = [&](int st) {
+          if (st < 16) return *(const bf16x8*)(buf + xor_at_use(qk_lat, 64 * (st & 3)) + 256 * (st >> 2));
+          return *(const bf16x8*)(buf + xor_at_use(qk_rope, 64 * (st - 16)));
+        };
+        // restart vote on tile it-2 (its softmax ran in the iteration before),
+        // read ahead of the K fragments so that its wait does not cover them
+        f32x4 vote = f32x4{};
+        if (it >= 2) vote = *(const f32x4*)sh.want[it & 1];
+        __builtin_amdgcn_sched_barrier(0);
+        bf16x8 kf[kPreQK];
         if (it < ntiles) {
-          const uint8_t* buf = ring(it);
-          f32x4 sacc[2] = {f32x4{}, f32x4{}};
-          auto kfrag = [&](int st) {
-            if (st < 16) return *(const bf16x8*)(buf + xor_at_use(qk_lat, 64 * (st & 3)) + 256 * (st >> 2));
-            return *(const bf16x8*)(buf + xor_at_use(qk_rope, 64 * (st - 16)));
-          };
-          bf16x8 kf[kPreQK];
 #pragma unroll
           for (int i = 0; i < kPreQK; ++i) kf[i] = kfrag(i);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if (it >= 1 && it <= ntiles) {
+          const int t = it - 1;
+          if (t == 0 && !have_ref) {
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb) m_ref[nb] = fmaxf(mprev[nb], sh.mt[0][w ^ 1][16 * nb + l16]);
+          }
+          // P in bf16, stored in the PV B-operand layout: block (ks = hf,
+          // rb = pr), lane L = j + 32*(q4 >> 1) holds keys 8*(q4 >> 1) .. +7 of
+          // row j; this lane's 4 keys are bytes 8*(q4 & 1) .. +7 of it
+          uint8_t* pbl = sh.pbuf[t & 1][2 * hf + pr];
+          bool want = false;
+#pragma unroll
+          for (int nb = 0; nb < 2; ++nb) {
+            float ps[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) ps[r] = __builtin_amdgcn_exp2f(fmaf(sprev[nb][r], a.scale_log2, -m_ref[nb]));
+            lsum[nb] += (ps[0] + ps[1]) + (ps[2] + ps[3]);
+            typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
+            bf16x4 pk;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) pk[r] = (__bf16)ps[r];
+            const int j = 16 * nb + l16;
+            *(bf16x4*)(pbl + (j + 32 * (q4 >> 1)) * 16 + 8 * (q4 & 1)) = pk;
+            want |= mprev[nb] > m_ref[nb] + kSlack;
+          }
+          const float wv = __any(want) ? 1.f : 0.f;
+          if (lane == 0) sh.want[t & 1][w] = wv;
+        }
+        if (it < ntiles) {
+          f32x4 sacc[2] = {f32x4{}, f32x4{}};
 #pragma unroll
           for (int st = 0; st < kQSteps; ++st) {
             const bf16x8 cur = kf[st % kPreQK];
@@ -317,51 +405,31 @@ __global__ __launch_bounds__(512, 1) void prefix_splitkv_kernel(PrefixArgs a) {
                 if (((vm >> (16 * hf + 4 * q4 + r)) & 1u) == 0) sacc[nb][r] = -INFINITY;
             }
           }
-          float mt[2];
 #pragma unroll
           for (int nb = 0; nb < 2; ++nb)
-            mt[nb] = max4(vmax(vmax(sacc[nb][0], sacc[nb][1]), vmax(sacc[nb][2], sacc[nb][3]))) * a.scale_log2;
+            mprev[nb] = max4(vmax(vmax(sacc[nb][0], sacc[nb][1]), vmax(sacc[nb][2], sacc[nb][3]))) * a.scale_log2;
           // the row max of this wave's 16 keys now sits in all four lanes of
           // the row; lanes 0..31 store it for row j = lane (nb = lane >> 4)
-          sh.mt[w][lane] = q4 == 0 ? mt[0] : mt[1];
-          if (it == 0 && !have_ref) {
-            lds_barrier();
-#pragma unroll
-            for (int nb = 0; nb < 2; ++nb) m_ref[nb] = fmaxf(mt[nb], sh.mt[w ^ 1][16 * nb + l16]);
-          }
-          // P in bf16, stored in the PV B-operand layout: block (ks = hf,
-          // rb = pr), lane L = j + 32*(q4 >> 1) holds keys 8*(q4 >> 1) .. +7 of
-          // row j; this lane's 4 keys are bytes 8*(q4 & 1) .. +7 of it
-          uint8_t* pbl = sh.pbuf[it & 1][2 * hf + pr];
-          bool want = false;
-#pragma unroll
-          for (int nb = 0; nb < 2; ++nb) {
-            float ps[4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) ps[r] = __builtin_amdgcn_exp2f(fmaf(sacc[nb][r], a.scale_log2, -m_ref[nb]));
-            lsum[nb] += (ps[0] + ps[1]) + (ps[2] + ps[3]);
-            typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
-            bf16x4 pk;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) pk[r] = (__bf16)ps[r];
-            const int j = 16 * nb + l16;
-            *(bf16x4*)(pbl + (j + 32 * (q4 >> 1)) * 16 + 8 * (q4 & 1)) = pk;
-            want |= mt[nb] > m_ref[nb] + kSlack;
-          }
-          const float wv = __any(want) ? 1.f : 0.f;
-          if (lane == 0) sh.want[it & 1][w] = wv;
+          sh.mt[mi][w][lane] = q4 == 0 ? mprev[0] : mprev[1];
+          sprev[0] = sacc[0];
+          sprev[1] = sacc[1];
         }
-        lds_barrier();
-        if (it < ntiles && sh.want[it & 1][0] + sh.want[it & 1][1] + sh.want[it & 1][2] + sh.want[it & 1][3] != 0.f) {
+        // restart vote on tile it-2, taken at the end of the iteration so
+        // that its LDS wait lands where the barrier waits anyway
+        if ((vote[0] + vote[1]) + (vote[2] + vote[3]) != 0.f) {
           restart = true;
+          restart_tile = it - 2;
           break;
         }
+        mi = mi == 2 ? 0 : mi + 1;
+        lds_barrier();
       }
       if (!restart) break;
       // restart with the pair's max over the offending tile plus headroom
+      const int bad = restart_tile % 3;
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) {
-        m_ref[nb] = fmaxf(m_ref[nb], fmaxf(sh.mt[w][16 * nb + l16], sh.mt[w ^ 1][16 * nb + l16])) + kSlack;
+        m_ref[nb] = fmaxf(m_ref[nb], fmaxf(sh.mt[bad][w][16 * nb + l16], sh.mt[bad][w ^ 1][16 * nb + l16])) + kSlack;
         lsum[nb] = 0.f;
       }
       have_ref = true;
@@ -370,11 +438,11 @@ __global__ __launch_bounds__(512, 1) void prefix_splitkv_kernel(PrefixArgs a) {
     // row sums: the four lanes of the row, then the partner wave
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) lsum[nb] = sum4(lsum[nb]);
-    sh.mt[w][lane] = q4 == 0 ? lsum[0] : lsum[1];
+    sh.mt[0][w][lane] = q4 == 0 ? lsum[0] : lsum[1];
     lds_barrier();
     if (hf == 0 && q4 < 2) {
       const int j = 32 * pr + lane;
-      const float l = sh.mt[w][lane] + sh.mt[w ^ 1][lane];
+      const float l = sh.mt[0][w][lane] + sh.mt[0][w ^ 1][lane];
       sh.rowl[j] = l;
       if (tile * kRowTile + j < rows_b) a.part_lse[pidx * kRowTile + j] = m_ref[q4] * kLn2 + logf(l);
     }
@@ -406,7 +474,6 @@ __global__ __launch_bounds__(512, 1) void prefix_splitkv_kernel(PrefixArgs a) {
     const int last = tree ? n_tree - 1 : kend - 1;
     return load_u32_async(list + min(base + 8 * c + (lane >> 3), last));
   };
-  bool have_ref = false;
   for (;;) {
     // Slot ring: svd holds the slots of tile it+2 (gathered in iteration it),
     // svn those of tile it+3.  Each iteration loads the next slots before its
@@ -427,47 +494,63 @@ __global__ __launch_bounds__(512, 1) void prefix_splitkv_kernel(PrefixArgs a) {
     }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    constexpr int kPrePV = 3;
-    auto vfrag_of = [&](const uint8_t* rbuf, int f) {
+    // V^T fragment f = 4ks + cb of a tile: two transposed reads at
+    // slot + vad[cb][hi] + 16384 ks
+    uint32_t vad[4][2];
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+      for (int hi = 0; hi < 2; ++hi) vad[cb][hi] = (uint32_t)(pvb[hi] ^ (64 * cb));
+    auto vread = [&](uint32_t slot, int f) {
       const int ks = f >> 2, cb = f & 3;
-      return tr_pair(rbuf, xor_at_use(pvb[0], 64 * cb) + ks * 16384, xor_at_use(pvb[1], 64 * cb) + ks * 16384);
+      const i16x4 lo = ds_tr(slot + vad[cb][0], ks * 16384);
+      const i16x4 hi = ds_tr(slot + vad[cb][1], ks * 16384);
+      return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
     };
+    const uint32_t pb_addr[2] = {lds_addr(sh.pbuf[0][0]) + 16 * lane, lds_addr(sh.pbuf[1][0]) + 16 * lane};
+    const uint32_t want_addr[2] = {lds_addr(sh.want[0]), lds_addr(sh.want[1])};
+    // V^T fragments: iteration it multiplies V(it-2) by P(it-2) and reads
+    // V(it-1) into each fragment register right after its last use
+    bf16x8 vf[8];
     bool restart = false;
-    for (int it = 0; it <= ntiles; ++it) {
-      if (it == 0 && !have_ref) lds_barrier();   // the QK waves' first-tile max exchange
+    for (int it = 0; it <= ntiles + 1; ++it) {
       const bool do_dma = it + 2 < ntiles;
       uint8_t* dbuf = ring(it + 2);
+      const uint32_t nslot = lds_addr(ring(max(it - 1, 0)));
       uint32_t svf = load_slot(it + 4);           // issued before this iteration's gathers
-      if (it >= 1) {
-        // PV of tile it-1, the gather of tile it+2 riding along
-        const uint8_t* rbuf = ring(it - 1);
-        const uint8_t* pbp = sh.pbuf[(it - 1) & 1][0];
+      f32x4 vote = f32x4{};
+      if (it >= 2) {
+        // LDS operations in issue order: vote, P0..P3, then two per fragment
+        vote = __builtin_bit_cast(f32x4, ds_b128(want_addr[it & 1], 0));
         bf16x8 pop[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) pop[i] = *(const bf16x8*)(pbp + i * 1024 + lane * 16);
-        // fragment f = 4ks + cb: V^T of columns block cb over key step ks,
-        // read kPrePV fragments ahead of its two MFMAs (one per row block)
-        auto vfrag = [&](int f) { return vfrag_of(rbuf, f); };
-        bf16x8 vf[kPrePV];
+        for (int i = 0; i < 4; ++i) pop[i] = ds_b128(pb_addr[it & 1], i * 1024);
+        // the gather of tile it+2 is issued while P(it-2) is in flight
+        if (do_dma) {
 #pragma unroll
-        for (int f = 0; f < kPrePV; ++f) vf[f] = vfrag(f);
+          for (int d = 0; d < 9; ++d) gather_one(a.pool, svd, dbuf, c, lane, d);
+        }
 #pragma unroll
         for (int f = 0; f < 8; ++f) {
           const int ks = f >> 2, cb = f & 3;
-          const bf16x8 av = vf[f % kPrePV];
-          if (f + kPrePV < 8) vf[f % kPrePV] = vfrag(f + kPrePV);
 #pragma unroll
           for (int rb = 0; rb < 2; ++rb) {
-            o[cb + 4 * rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pop[2 * ks + rb], o[cb + 4 * rb], 0, 0, 0);
-            const int g = 2 * f + rb;
-            if (do_dma && (g & 1) == 0) gather_one(a.pool, svd, dbuf, c, lane, g >> 1);
+            const int j = 2 * ks + rb;
+            if (cb == 0) wait_lgkm((3 - j) + 2 * f, pop[j]);
+            o[cb + 4 * rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[f], pop[j], o[cb + 4 * rb], 0, 0, 0);
+            if (rb == 1) vf[f] = vread(nslot, f);  // V(it-1); at it = ntiles+1 a harmless re-read
             __builtin_amdgcn_sched_barrier(0);
           }
         }
-        if (do_dma) gather_one(a.pool, svd, dbuf, c, lane, 8);
-      } else if (do_dma) {
+      } else {
+        if (it == 1) {
 #pragma unroll
-        for (int d = 0; d < 9; ++d) gather_one(a.pool, svd, dbuf, c, lane, d);
+          for (int f = 0; f < 8; ++f) vf[f] = vread(nslot, f);
+        }
+        if (do_dma) {
+#pragma unroll
+          for (int d = 0; d < 9; ++d) gather_one(a.pool, svd, dbuf, c, lane, d);
+        }
       }
       // the gather of tile it+1 (issued one iteration ago) and the slot load
       // above must have landed; this iteration's nine gathers may stay in
@@ -476,17 +559,23 @@ __global__ __launch_bounds__(512, 1) void prefix_splitkv_kernel(PrefixArgs a) {
       else asm volatile("s_waitcnt vmcnt(0)" : "+v"(svf) :: "memory");
       svd = svn;
       svn = svf;
-      lds_barrier();
-      if (it < ntiles && sh.want[it & 1][0] + sh.want[it & 1][1] + sh.want[it & 1][2] + sh.want[it & 1][3] != 0.f) {
+      // V(it-1) reads landed (and named, for their next use) before the barrier
+      // after which their slot may be refilled
+      asm volatile("s_waitcnt lgkmcnt(0)"
+                   : "+v"(vote), "+v"(vf[0]), "+v"(vf[1]), "+v"(vf[2]), "+v"(vf[3]), "+v"(vf[4]), "+v"(vf[5]),
+                     "+v"(vf[6]), "+v"(vf[7])
+                   :
+                   : "memory");
+      if ((vote[0] + vote[1]) + (vote[2] + vote[3]) != 0.f) {   // restart vote on tile it-2
         restart = true;
         break;
       }
+      asm volatile("s_barrier" ::: "memory");
     }
     if (!restart) break;
     __builtin_amdgcn_s_waitcnt(0);
 #pragma unroll
     for (int d = 0; d < 8; ++d) o[d] = f32x16{};
-    have_ref = true;
     __syncthreads();
   }
   lds_barrier();                                  // QK waves publish row sums
