@@ -43,8 +43,10 @@ __global__ __launch_bounds__(kRowTile * kGroups) void lse_merge_kernel(MergeArgs
   const float4* o_p = (const float4*)a.part_o + (p0 * kD4 + d4) * kRowTile + rit;
   const size_t o_stride = (size_t)kD4 * kRowTile;          // float4s per chunk partial
 
+  // One round trip: the chunks' lse values and partials are loaded
+  // together, the max is taken from registers.  Requests with more chunks
+  // than fit in one batch fold their batches with a running max.
   float m = -INFINITY;
-  for (int s = 0; s < S; ++s) m = fmaxf(m, lse_p[s * kRowTile]);
   float sum = 0.f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   for (int s0 = 0; s0 < S; s0 += kMaxMergeUnroll) {
@@ -56,6 +58,19 @@ __global__ __launch_bounds__(kRowTile * kGroups) void lse_merge_kernel(MergeArgs
         v[j] = o_p[(size_t)(s0 + j) * o_stride];
         w[j] = lse_p[(s0 + j) * kRowTile];
       }
+    }
+    float mb = m;
+#pragma unroll
+    for (int j = 0; j < kMaxMergeUnroll; ++j)
+      if (s0 + j < S) mb = fmaxf(mb, w[j]);
+    if (mb > m) {                    // rescale what earlier batches summed
+      const float c = __expf(m - mb);
+      sum *= c;
+      acc.x *= c;
+      acc.y *= c;
+      acc.z *= c;
+      acc.w *= c;
+      m = mb;
     }
 #pragma unroll
     for (int j = 0; j < kMaxMergeUnroll; ++j) {

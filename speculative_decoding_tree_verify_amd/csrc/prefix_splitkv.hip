@@ -233,10 +233,9 @@ __device__ __forceinline__ void gather_one(const uint16_t* pool, uint32_t sv, ui
 
 struct Shared {
   uint8_t pbuf[2][4][1024];                   // P operands, [parity][ks*2 + rb][lane*16]
-  float mt[3][4][64];                         // QK waves: row max of the tile, by tile index mod 3
+  float2 mtl[3][4][64];                       // QK waves: per-lane max of each 16-row half, by tile mod 3
   float want[2][4];                           // QK waves: restart vote per tile parity
   float rowl[64];                             // final row sums (QK -> PV)
-  float rowm[64];                             // final row references
   uint32_t vis[kRowTile][4];                  // tree masks: bit k of word tt = tree key 32tt + k visible
   int par[kMaxTree];
 };
@@ -323,6 +322,17 @@ __global__ __launch_bounds__(512, 1) void prefix_splitkv_kernel(PrefixArgs a) {
     float lsum[2] = {0.f, 0.f};
     bool have_ref = false;
     int restart_tile = 0;
+    // max of row 16nb + l16 of the pair over tile slot k: its four lanes in
+    // this wave and in the partner wave
+    auto pair_row_max = [&](int k, int nb) {
+      float m = -INFINITY;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float2 u = sh.mtl[k][w][16 * q + l16], v = sh.mtl[k][w ^ 1][16 * q + l16];
+        m = fmaxf(m, fmaxf(nb ? u.y : u.x, nb ? v.y : v.x));
+      }
+      return m;
+    };
     for (;;) {                                 // again after a restart
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();                         // prologue: tiles 0, 1 staged
@@ -334,10 +344,17 @@ __global__ __launch_bounds__(512, 1) void prefix_splitkv_kernel(PrefixArgs a) {
       int mi = 0;                            // it mod 3
       float mprev[2] = {0.f, 0.f};           // their row max (log2 units), this wave's keys
       for (int it = 0; it <= ntiles + 1; ++it) {
-        const uint8_t* buf = ring(it);
+        typedef __attribute__((address_space(3))) const bf16x8 lds_frag;
+        const uint32_t slot = lds_addr(ring(it));
+        const lds_frag* kp[4];
+        const lds_frag* kpr[2];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) kp[j] = (const lds_frag*)(uintptr_t)(slot + (uint32_t)(qk_lat ^ (64 * j)));
+#pragma unroll
+        for (int j = 0; j < 2; ++j) kpr[j] = (const lds_frag*)(uintptr_t)(slot + (uint32_t)(qk_rope ^ (64 * j)));
         auto kfrag = [&](int st) {
-          if (st < 16) return *(const bf16x8*)(buf + xor_at_use(qk_lat, 64 * (st & 3)) + 256 * (st >> 2));
-          return *(const bf16x8*)(buf + xor_at_use(qk_rope, 64 * (st - 16)));
+          if (st < 16) return kp[st & 3][16 * (st >> 2)];
+          return kpr[st - 16][0];
         };
         // restart vote on tile it-2 (its softmax ran in the iteration before),
         // read ahead of the K fragments so that its wait does not cover them
@@ -354,7 +371,7 @@ __global__ __launch_bounds__(512, 1) void prefix_splitkv_kernel(PrefixArgs a) {
           const int t = it - 1;
           if (t == 0 && !have_ref) {
 #pragma unroll
-            for (int nb = 0; nb < 2; ++nb) m_ref[nb] = fmaxf(mprev[nb], sh.mt[0][w ^ 1][16 * nb + l16]);
+            for (int nb = 0; nb < 2; ++nb) m_ref[nb] = pair_row_max(0, nb);
           }
           // P in bf16, stored in the PV B-operand layout: block (ks = hf,
           // rb = pr), lane L = j + 32*(q4 >> 1) holds keys 8*(q4 >> 1) .. +7 of
@@ -405,12 +422,14 @@ __global__ __launch_bounds__(512, 1) void prefix_splitkv_kernel(PrefixArgs a) {
                 if (((vm >> (16 * hf + 4 * q4 + r)) & 1u) == 0) sacc[nb][r] = -INFINITY;
             }
           }
+          // this lane's max over its 4 keys of each row (log2 units): a row
+          // breaks the reference iff one of its lanes does, so the restart
+          // test needs no cross-lane reduction; the row max itself is
+          // reduced only on the rare paths (first tile, restart)
 #pragma unroll
           for (int nb = 0; nb < 2; ++nb)
-            mprev[nb] = max4(vmax(vmax(sacc[nb][0], sacc[nb][1]), vmax(sacc[nb][2], sacc[nb][3]))) * a.scale_log2;
-          // the row max of this wave's 16 keys now sits in all four lanes of
-          // the row; lanes 0..31 store it for row j = lane (nb = lane >> 4)
-          sh.mt[mi][w][lane] = q4 == 0 ? mprev[0] : mprev[1];
+            mprev[nb] = vmax(vmax(sacc[nb][0], sacc[nb][1]), vmax(sacc[nb][2], sacc[nb][3])) * a.scale_log2;
+          sh.mtl[mi][w][lane] = make_float2(mprev[0], mprev[1]);
           sprev[0] = sacc[0];
           sprev[1] = sacc[1];
         }
@@ -429,7 +448,7 @@ __global__ __launch_bounds__(512, 1) void prefix_splitkv_kernel(PrefixArgs a) {
       const int bad = restart_tile % 3;
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) {
-        m_ref[nb] = fmaxf(m_ref[nb], fmaxf(sh.mt[bad][w][16 * nb + l16], sh.mt[bad][w ^ 1][16 * nb + l16])) + kSlack;
+        m_ref[nb] = fmaxf(m_ref[nb], pair_row_max(bad, nb)) + kSlack;
         lsum[nb] = 0.f;
       }
       have_ref = true;
@@ -438,11 +457,11 @@ __global__ __launch_bounds__(512, 1) void prefix_splitkv_kernel(PrefixArgs a) {
     // row sums: the four lanes of the row, then the partner wave
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) lsum[nb] = sum4(lsum[nb]);
-    sh.mt[0][w][lane] = q4 == 0 ? lsum[0] : lsum[1];
+    sh.mtl[0][w][lane].x = q4 == 0 ? lsum[0] : lsum[1];
     lds_barrier();
     if (hf == 0 && q4 < 2) {
       const int j = 32 * pr + lane;
-      const float l = sh.mt[0][w][lane] + sh.mt[0][w ^ 1][lane];
+      const float l = sh.mtl[0][w][lane].x + sh.mtl[0][w ^ 1][lane].x;
       sh.rowl[j] = l;
       if (tile * kRowTile + j < rows_b) a.part_lse[pidx * kRowTile + j] = m_ref[q4] * kLn2 + logf(l);
     }

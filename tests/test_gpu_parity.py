@@ -88,16 +88,19 @@ def test_sharp_scores_move_the_reference():
     check(x, chunk=1024, what="sharp scores")
 
 
-def test_reference_jump_mid_chunk():
+@pytest.mark.parametrize("chunk", [2048, 64])
+def test_reference_jump_mid_chunk(chunk):
     # one prefix key deep inside a chunk gets a score far above everything
-    # before it, so the running reference max has to move mid-chunk
+    # before it, so the running reference max has to move mid-chunk; with
+    # 64-key chunks the key sits in chunk 23 of 32, past the merge's first
+    # batch of 16 partials, so the merge's running max moves too
     rng = np.random.default_rng(7)
     x = small([2000], [gen.random_tree(5, rng)], 2, seed=19)
     key = 1500
     slot = x.prefix_slot_idx[key]
     k = vo.bf16_bits_to_f64(x.pool[slot])
     x.q[2, 1] = gen.f32_to_bf16_bits((k * 40.0).astype(np.float32))                  # score ~ 40*|k|^2*sigma
-    out, lse = check(x, chunk=2048, what="reference jump")
+    out, lse = check(x, chunk=chunk, what=f"reference jump chunk={chunk}")
     np.testing.assert_allclose(out[2, 1], k[:512], atol=2e-2)
 
 
