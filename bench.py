@@ -16,6 +16,12 @@ Prints ONE JSON line (stdout):
 Details go to stderr.
 
   python bench.py [--steps K] [--warmup W] [--config 1..5] [--no-cpu]
+                  [--slot-mode scrambled|contiguous|churned]
+
+Besides the mean over the K timed steps, stderr and `config` carry per-step
+percentiles (HIP events around each step), the same steps with one pool copy
+(KV warm in the Infinity Cache), and the effective KV rate as a fraction of a
+measured device-copy rate.
 """
 
 from __future__ import annotations
@@ -57,6 +63,21 @@ def err(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+METRIC_WORKLOAD = {3: "64k prefix, 65 nodes"}
+
+
+def roofline_of_split(mfma_bound: bool, flops: float, alg: dict, ms_split: float, traffic):
+    """The split kernel against the roofline that binds the workload: bf16
+    MFMA when its algorithmic flops take longer at peak than its algorithmic
+    bytes (KV rows and queries read once), HBM otherwise."""
+    if mfma_bound:
+        achieved, peak, unit = flops / (ms_split * 1e-3) / 1e12, MFMA_BF16_PEAK_TFLOPS, "TFLOP/s"
+    else:
+        achieved, peak, unit = alg["split_bytes"] / (ms_split * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s"
+    return {"bound": "mfma" if mfma_bound else "hbm", "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+            "frac": round(achieved / peak, 4), "traffic": traffic, "traffic_unit": "bytes per launch"}
+
+
 def workload_name(k: int) -> str:
     return gen.CONFIG_NAMES[k]
 
@@ -76,7 +97,7 @@ def algorithmic(x: gen.VerifyInputs):
     T = x.total_tree
     io_bytes = T * H * (KV_ROW_BYTES + 512 * 2 + 4)
     return dict(kv_bytes=kv_rows * KV_ROW_BYTES, prefix_flops=prefix_flops, tail_flops=tail_flops,
-                io_bytes=io_bytes)
+                io_bytes=io_bytes, split_bytes=kv_rows * KV_ROW_BYTES + T * H * KV_ROW_BYTES)
 
 
 def split_kernel_traffic():
@@ -90,6 +111,40 @@ def split_kernel_traffic():
         return None
     fetch_kib, write_kib, fs, ws = m
     return int(round((fetch_kib * fs + write_kib * ws) * 1024))
+
+
+def step_percentiles(fn, iters: int):
+    """p10 / p50 / p90 of single-call durations (us), each call bracketed by
+    its own pair of events on the launch stream."""
+    import torch
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
+    torch.cuda.synchronize()
+    for i, (a, b) in enumerate(evs):
+        a.record()
+        fn(i)
+        b.record()
+    torch.cuda.synchronize()
+    us = np.array([a.elapsed_time(b) * 1e3 for a, b in evs])
+    return [round(float(np.percentile(us, q)), 2) for q in (10, 50, 90)]
+
+
+def copy_rate_gbs(nbytes: int = 1 << 30, iters: int = 10) -> float:
+    """Device-to-device copy rate (bytes read + written per second), GB/s."""
+    import torch
+    a = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    b.copy_(a)
+    s = torch.cuda.Event(enable_timing=True)
+    e = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    s.record()
+    for _ in range(iters):
+        b.copy_(a)
+    e.record()
+    torch.cuda.synchronize()
+    rate = 2 * nbytes * iters / (s.elapsed_time(e) * 1e-3) / 1e9
+    del a, b
+    return rate
 
 
 def time_events(fn, iters: int) -> float:
@@ -136,6 +191,8 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--config", type=int, default=3)
+    ap.add_argument("--slot-mode", default=None, choices=["scrambled", "contiguous", "churned"],
+                    help="slot layout of the pool (default: the workload's own)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 512 MiB device copy (counter calibration under rocprofv3 --pmc)")
@@ -153,8 +210,9 @@ def main():
     vb.lib()   # fail loudly if the HIP library is missing
 
     t0 = time.perf_counter()
-    x = gen.config_inputs(args.config)
-    err(f"[bench] workload: {workload_name(args.config)}  (inputs generated in {time.perf_counter() - t0:.1f} s)")
+    x = gen.config_inputs(args.config, slot_mode=args.slot_mode)
+    wname = workload_name(args.config) + (f", {args.slot_mode} slots" if args.slot_mode else "")
+    err(f"[bench] workload: {wname}  (inputs generated in {time.perf_counter() - t0:.1f} s)")
     alg = algorithmic(x)
     prob = vb.Problem.from_host(x.cu_prefix, x.cu_tree, x.num_heads, x.pool.shape[0], x.scale)
     info = vb.plan(prob)
@@ -205,13 +263,21 @@ def main():
     ms_split = time_events(split_only, iters)
     ms_merge = time_events(merge_only, iters)
     ms_step_ev = time_events(step, iters)
+    pct = warm = copy_gbs = None
+    if not args.calib_copy:   # counter runs keep to the copies they calibrate against
+        pct = step_percentiles(step, iters)
+        warm = step_percentiles(lambda i: step(0), iters)
+        copy_gbs = copy_rate_gbs()
+        err(f"[bench] per-step us p10/p50/p90: {pct} (pool copies rotated), {warm} (one pool copy, warm); "
+            f"device copy {copy_gbs:.0f} GB/s")
     # algorithmic flops of the split kernel: every (row, visible key) pair, prefix and tree
-    achieved = (alg["prefix_flops"] + alg["tail_flops"]) / (ms_split * 1e-3) / 1e12
+    flops = alg["prefix_flops"] + alg["tail_flops"]
+    achieved = flops / (ms_split * 1e-3) / 1e12
     err(f"[bench] step {ms_per_step * 1e3:.1f} us (wall), {ms_step_ev * 1e3:.1f} us (events); "
         f"split {ms_split * 1e3:.1f} us, merge {ms_merge * 1e3:.1f} us")
     err(f"[bench] split kernel {achieved:.1f} TFLOP/s = {achieved / MFMA_BF16_PEAK_TFLOPS * 100:.1f}% of bf16 "
         f"MFMA peak; effective KV {value:.1f} GB/s = {value / HBM_PEAK_GBS * 100:.2f}% of HBM peak")
-    t_mfma = (alg["prefix_flops"] + alg["tail_flops"]) / (MFMA_BF16_PEAK_TFLOPS * 1e12)
+    t_mfma = flops / (MFMA_BF16_PEAK_TFLOPS * 1e12)
     t_hbm = (alg["kv_bytes"] + alg["io_bytes"]) / (HBM_PEAK_GBS * 1e9)
     err(f"[bench] roofline bounds per step: MFMA {t_mfma * 1e6:.1f} us, HBM {t_hbm * 1e6:.1f} us; "
         f"fraction of binding roofline {max(t_mfma, t_hbm) / (ms_per_step * 1e-3):.3f}")
@@ -231,7 +297,7 @@ def main():
         err(f"[bench] cpu oracle: {cpu['ms_per_step']:.1f} ms/step on {cpu['cores']} threads")
 
     rec = {
-        "metric": "effective KV-read GB/s (% HBM peak) + us per verify step, 64k prefix, 65 nodes",
+        "metric": "effective KV-read GB/s (% HBM peak) + us per verify step, " + METRIC_WORKLOAD.get(args.config, wname),
         "value": round(value, 2),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -244,23 +310,20 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {
-            "workload": workload_name(args.config),
+            "workload": wname,
             "batch": x.batch, "heads": x.num_heads, "prefix": x.total_prefix, "tree_nodes": x.total_tree,
             "pool_slots": int(x.pool.shape[0]), "kv_bytes": alg["kv_bytes"],
             "us_per_step": round(ms_per_step * 1e3, 2),
             "pct_hbm_peak": round(value / HBM_PEAK_GBS * 100, 3),
             "kernel_us": {"prefix_splitkv": round(ms_split * 1e3, 2), "lse_merge": round(ms_merge * 1e3, 2)},
             "binding_roofline_fraction": round(max(t_mfma, t_hbm) / (ms_per_step * 1e-3), 4),
+            "step_us_p10_p50_p90": pct,
+            "step_us_warm_p10_p50_p90": warm,
+            "device_copy_gbs": round(copy_gbs, 1) if copy_gbs else None,
+            "pct_of_device_copy": round(value / copy_gbs * 100, 3) if copy_gbs else None,
         },
-        "roofline": {
-            "bound": "mfma",
-            "achieved": round(achieved, 2),
-            "peak": MFMA_BF16_PEAK_TFLOPS,
-            "unit": "TFLOP/s",
-            "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
-            "traffic": split_kernel_traffic(),
-            "traffic_unit": "bytes per launch",
-        },
+        "roofline": roofline_of_split(t_mfma >= t_hbm, flops, alg, ms_split,
+                                      split_kernel_traffic() if args.config == 3 and not args.slot_mode else None),
         "cpu_baseline": ({k: v for k, v in cpu.items() if k != "ms_per_step"} if cpu else None),
     }
     print(json.dumps(rec), flush=True)

@@ -80,6 +80,7 @@ constexpr int kQSteps = kDqk / 32;            // 18 steps of v_mfma_f32_16x16x32
 constexpr int kPreQK = 4;                     // K fragments read ahead
 constexpr int kRsrcWord3 = 0x00020000;
 constexpr int kMaxTreeTiles = (kMaxTree + kKT - 1) / kKT;   // 3
+constexpr int kCompactBatch = 64;             // requests scanned per workgroup to list real items
 
 __device__ __forceinline__ int swz_latent(int k) { return ((k & 3) << 2) | ((k >> 2) & 3); }
 __device__ __forceinline__ int swz_rope(int k) { return (k >> 1) & 7; }
@@ -255,21 +256,54 @@ __global__ __launch_bounds__(512, 1) void prefix_splitkv_kernel(PrefixArgs a) {
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const bool is_qk = w < 4;
 
-  // work item (same decomposition as the 4-wave kernel)
-  const int per_xcd = a.grid_items >> 3;
-  const int k = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
-  const int tiles_chunks = a.row_tiles * a.max_chunks;
-  if (k >= a.batch * tiles_chunks) return;
-  const int b = k / tiles_chunks;
-  const int rem = k - b * tiles_chunks;
-  const int s = rem / a.row_tiles;
-  const int tile = rem - s * a.row_tiles;
+  // Work item -> (request b, chunk s, row tile).  Real items are listed in
+  // request order, a chunk's row tiles consecutive; XCD x (= blockIdx % 8,
+  // the round-robin dispatch) takes the x-th contiguous eighth of the list,
+  // so the row tiles of a chunk share an XCD's L2 and every XCD gets the same
+  // number of items however unequal the requests are.  Requests with no tree
+  // node have no items.  Past kCompactBatch requests the per-workgroup scan
+  // would cost more than it saves, and the padded grid is used as it is.
+  int b, s, tile;
+  const int chunk = a.chunk, max_chunks = a.max_chunks;
+  auto nch_of = [&](int L) { return max(1, min((L + chunk - 1) / chunk, max_chunks)); };
+  if (a.batch <= kCompactBatch) {
+    auto items_of = [&](int i) {
+      const int L_i = a.cu_prefix[i + 1] - a.cu_prefix[i];
+      const int rt = min((( a.cu_tree[i + 1] - a.cu_tree[i]) * a.num_heads + kRowTile - 1) / kRowTile, a.row_tiles);
+      return __builtin_amdgcn_readfirstlane(nch_of(L_i) * max(rt, 0));
+    };
+    int total = 0;
+    for (int i = 0; i < a.batch; ++i) total += items_of(i);
+    const int per_xcd = (total + 7) >> 3;
+    const int j = blockIdx.x >> 3;
+    int r = (blockIdx.x & 7) * per_xcd + j;
+    if (j >= per_xcd || r >= total) return;
+    b = 0;
+    for (;;) {
+      const int n = items_of(b);
+      if (r < n) break;
+      r -= n;
+      ++b;
+    }
+    const int rt_b = min(((a.cu_tree[b + 1] - a.cu_tree[b]) * a.num_heads + kRowTile - 1) / kRowTile, a.row_tiles);
+    s = r / rt_b;
+    tile = r - s * rt_b;
+  } else {
+    const int per_xcd = a.grid_items >> 3;
+    const int k = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+    const int tiles_chunks = a.row_tiles * max_chunks;
+    if (k >= a.batch * tiles_chunks) return;
+    b = k / tiles_chunks;
+    const int rem = k - b * tiles_chunks;
+    s = rem / a.row_tiles;
+    tile = rem - s * a.row_tiles;
+  }
   const int p0 = a.cu_prefix[b];
   const int L = a.cu_prefix[b + 1] - p0;
-  const int nchunks = max(1, min((L + a.chunk - 1) / a.chunk, a.max_chunks));
+  const int nchunks = nch_of(L);
   if (s >= nchunks) return;
-  const int kbeg = s * a.chunk;
-  const int kend = min(kbeg + a.chunk, L);
+  const int kbeg = s * chunk;
+  const int kend = min(kbeg + chunk, L);
   const int t0 = a.cu_tree[b];
   const int n_b = a.cu_tree[b + 1] - t0;
   const int rows_b = n_b * a.num_heads;
