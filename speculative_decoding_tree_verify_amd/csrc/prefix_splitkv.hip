@@ -312,6 +312,7 @@ __global__ __launch_bounds__(512, 1) void prefix_splitkv_kernel(PrefixArgs a) {
   const int ntp = kend > kbeg ? (kend - kbeg + kKT - 1) / kKT : 0;
   const int ntt = s == nchunks - 1 ? (n_tree + kKT - 1) / kKT : 0;
   const int ntiles = ntp + ntt;
+  const int nfull = (kend - kbeg) / kKT;           // prefix tiles with all 32 keys
 
   if (ntt > 0) {
     for (int i = threadIdx.x; i < n_tree; i += blockDim.x) sh.par[i] = a.parent[t0 + i];
@@ -426,8 +427,8 @@ __global__ __launch_bounds__(512, 1) void prefix_splitkv_kernel(PrefixArgs a) {
             *(bf16x4*)(pbl + (j + 32 * (q4 >> 1)) * 16 + 8 * (q4 & 1)) = pk;
             want |= mprev[nb] > m_ref[nb] + kSlack;
           }
-          const float wv = __any(want) ? 1.f : 0.f;
-          if (lane == 0) sh.want[t & 1][w] = wv;
+          // every lane stores the wave's vote (same value, same address)
+          sh.want[t & 1][w] = __any(want) ? 1.f : 0.f;
         }
         if (it < ntiles) {
           f32x4 sacc[2] = {f32x4{}, f32x4{}};
@@ -440,20 +441,23 @@ __global__ __launch_bounds__(512, 1) void prefix_splitkv_kernel(PrefixArgs a) {
             __builtin_amdgcn_sched_barrier(0);
           }
           // lane holds keys 16hf + 4q4 + r (r = 0..3) of rows 32pr + 16nb + l16
-          const bool tree = it >= ntp;
-          const int nvalid = tree ? kKT : min(kKT, kend - kbeg - it * kKT);
+          // masks only on the last prefix tile (ragged) and the tree tiles
+          if (it >= nfull) {
+            const bool tree = it >= ntp;
+            const int nvalid = tree ? kKT : min(kKT, kend - kbeg - it * kKT);
 #pragma unroll
-          for (int nb = 0; nb < 2; ++nb) {
-            if (nvalid < kKT) {
+            for (int nb = 0; nb < 2; ++nb) {
+              if (nvalid < kKT) {
 #pragma unroll
-              for (int r = 0; r < 4; ++r)
-                if (16 * hf + 4 * q4 + r >= nvalid) sacc[nb][r] = -INFINITY;
-            }
-            if (tree) {
-              const uint32_t vm = sh.vis[32 * pr + 16 * nb + l16][it - ntp];
+                for (int r = 0; r < 4; ++r)
+                  if (16 * hf + 4 * q4 + r >= nvalid) sacc[nb][r] = -INFINITY;
+              }
+              if (tree) {
+                const uint32_t vm = sh.vis[32 * pr + 16 * nb + l16][it - ntp];
 #pragma unroll
-              for (int r = 0; r < 4; ++r)
-                if (((vm >> (16 * hf + 4 * q4 + r)) & 1u) == 0) sacc[nb][r] = -INFINITY;
+                for (int r = 0; r < 4; ++r)
+                  if (((vm >> (16 * hf + 4 * q4 + r)) & 1u) == 0) sacc[nb][r] = -INFINITY;
+              }
             }
           }
           // this lane's max over its 4 keys of each row (log2 units): a row
@@ -545,7 +549,10 @@ __global__ __launch_bounds__(512, 1) void prefix_splitkv_kernel(PrefixArgs a) {
         for (int d = 0; d < 9; ++d) gather_one(a.pool, s1, tile1, c, lane, d);
       }
     }
-    __builtin_amdgcn_s_waitcnt(0);
+    // tile 0 must have landed; tile 1's nine gathers may stay in flight
+    // (iteration 0's closing wait covers them)
+    if (ntiles > 1) asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     // V^T fragment f = 4ks + cb of a tile: two transposed reads at
     // slot + vad[cb][hi] + 16384 ks
