@@ -60,7 +60,7 @@ extern "C" {
 #define VAMLA_D_V 512           /* V = columns [0, 512) of the same row */
 #define VAMLA_MAX_TREE 65       /* root + up to 64 drafted nodes */
 #define VAMLA_MAX_HEADS 128
-#define VAMLA_KEY_TILE 64       /* chunk sizes are multiples of this */
+#define VAMLA_KEY_TILE 32       /* chunk sizes are multiples of this */
 #define VAMLA_ROW_TILE 64       /* query rows per prefix work item */
 
 typedef enum vamla_status {
@@ -94,7 +94,7 @@ typedef struct vamla_params {
   int32_t total_tree;       /* T = cu_tree[B] >= 1 */
   int64_t max_prefix;       /* >= every L_b (planning bound), >= 0 */
   int64_t total_prefix;     /* cu_prefix[B]; used to choose the chunk size */
-  int32_t chunk;            /* prefix keys per split; multiple of 64, or 0 = choose automatically */
+  int32_t chunk;            /* prefix keys per split; multiple of 32, or 0 = choose automatically */
   uint32_t flags;           /* reserved, must be 0 */
   const int32_t* cu_prefix; /* device [B+1], cu_prefix[0] = 0, non-decreasing */
   const int32_t* cu_tree;   /* device [B+1], cu_tree[0] = 0, increasing (N_b >= 1) */
@@ -104,7 +104,7 @@ typedef struct vamla_params {
 
 /* Work decomposition the library derives from vamla_params (host only). */
 typedef struct vamla_plan_info {
-  int32_t chunk;            /* prefix keys per split (multiple of 64) */
+  int32_t chunk;            /* prefix keys per split (multiple of 32) */
   int32_t row_tiles;        /* ceil(max_tree * H / 64): row tiles per request */
   int32_t max_chunks;       /* ceil(max_prefix / chunk), >= 1 */
   int32_t grid_items;       /* split kernel grid (B * row_tiles * max_chunks, padded to 8) */

@@ -21,7 +21,7 @@ D_QK = 576
 D_V = 512
 MAX_TREE = 65
 MAX_HEADS = 128
-KEY_TILE = 64
+KEY_TILE = 32
 ROW_TILE = 64
 
 STATUS = {

@@ -11,7 +11,7 @@ namespace vamla {
 constexpr int kDqk = 576;                  // latent 512 + rope 64
 constexpr int kDv = 512;
 constexpr int kChunks16 = kDqk / 8;        // 72 sixteen-byte pieces per pool row
-constexpr int kKeyTile = 64;               // chunk sizes are multiples of this
+constexpr int kKeyTile = 32;               // chunk sizes are multiples of this (the key tile)
 constexpr int kRowTile = 64;               // query rows per split work item
 constexpr int kD4 = kDv / 4;               // 128 float4 groups per output row
 constexpr int kMaxTree = 65;

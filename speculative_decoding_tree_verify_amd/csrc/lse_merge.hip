@@ -22,7 +22,7 @@ namespace vamla {
 namespace {
 
 constexpr int kGroups = 4;          // float4 column groups per workgroup
-constexpr int kMaxMergeUnroll = 16; // chunks whose loads are issued together
+constexpr int kMaxMergeUnroll = 32; // chunks whose loads are issued together
 
 __global__ __launch_bounds__(kRowTile * kGroups) void lse_merge_kernel(MergeArgs a) {
   const int item = blockIdx.x;

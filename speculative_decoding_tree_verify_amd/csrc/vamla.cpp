@@ -27,9 +27,12 @@ static_assert(VAMLA_MAX_TREE == kMaxTree && VAMLA_MAX_HEADS == kMaxHeads, "heade
 // Chunk choice assumes the full MI355X: 256 CUs, one prefix work item per CU
 // at a time (the item's key tiles fill the LDS).
 constexpr int64_t kCUs = 256;
-// Fixed cost of one prefix work item (loading its queries, writing its
-// partial), expressed in keys of streaming work.
+// Fixed cost of one prefix work item (loading its queries, the first key
+// tiles' round trips), expressed in keys of streaming work.
 constexpr int64_t kItemOverheadKeys = 256;
+// Cost of one item's partial (64 rows x 2 KB written by the split pass and
+// read back by the merge) at the chip's write + read rate, in the same units.
+constexpr int64_t kPartialKeys = 2;
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
@@ -61,7 +64,9 @@ int64_t choose_chunk(const vamla_params* p, int64_t row_tiles) {
   // the last chunk of a request also streams its tree keys (whole tiles)
   const int64_t tree_keys = ceil_div(p->max_tree, VAMLA_KEY_TILE) * VAMLA_KEY_TILE;
   // Candidates: the longest prefix split into k chunks, k = 1, 2, ...; cost =
-  // rounds of work items over the CUs times the keys the largest item streams.
+  // rounds of work items over the CUs times the keys the largest item
+  // streams, plus the partials' traffic (which makes small problems prefer
+  // fewer, longer chunks).
   int64_t best_c = VAMLA_KEY_TILE, best_cost = INT64_MAX;
   const int64_t kmax = std::min<int64_t>(ceil_div(maxL, VAMLA_KEY_TILE), 8192);
   for (int64_t k = 1; k <= kmax; ++k) {
@@ -73,7 +78,7 @@ int64_t choose_chunk(const vamla_params* p, int64_t row_tiles) {
     const int64_t rounds = ceil_div(items, kCUs);
     const int64_t last = maxL - (ceil_div(maxL, c) - 1) * c;
     const int64_t item_keys = std::max(c, ceil_div(last, VAMLA_KEY_TILE) * VAMLA_KEY_TILE + tree_keys);
-    const int64_t cost = rounds * (item_keys + kItemOverheadKeys);
+    const int64_t cost = rounds * (item_keys + kItemOverheadKeys) + items * kPartialKeys;
     if (cost < best_cost || (cost == best_cost && c > best_c)) {   // ties: larger chunk, fewer partials
       best_cost = cost;
       best_c = c;

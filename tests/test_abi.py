@@ -63,7 +63,7 @@ def prob(k):
 def test_plan_covers_the_problem(L, k):
     p = prob(k)
     info = vb.plan(p)
-    assert info.chunk % 64 == 0 and info.chunk >= 64
+    assert info.chunk % 32 == 0 and info.chunk >= 32
     assert info.row_tiles == math.ceil(p.max_tree * p.num_heads / 64)
     assert info.max_chunks * info.chunk >= p.max_prefix
     assert (info.max_chunks - 1) * info.chunk < max(p.max_prefix, 1)
@@ -81,16 +81,16 @@ def test_plan_fills_the_chip_for_the_64k_config(L):
     info = vb.plan(p)
     items = info.row_tiles * info.max_chunks
     assert 200 <= items <= 256        # one round of work items over 256 CUs
-    # the last chunk also streams the tree's two key tiles; it must not be the longest item
+    # the last chunk also streams the tree's three 32-key tiles; it must not be the longest item
     last = p.max_prefix - (info.max_chunks - 1) * info.chunk
-    assert math.ceil(last / 64) * 64 + 128 <= info.chunk
+    assert math.ceil(last / 32) * 32 + 96 <= info.chunk
 
 
 def test_explicit_chunk_is_kept(L):
     p = prob(2)
     p.chunk = 512
     assert vb.plan(p).chunk == 512
-    p.chunk = 100                      # not a multiple of 64
+    p.chunk = 100                      # not a multiple of the 32-key tile
     with pytest.raises(vb.VamlaError) as e:
         vb.plan(p)
     assert e.value.status == -1

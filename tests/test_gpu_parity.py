@@ -61,6 +61,17 @@ def test_batch_varlen_with_empty_prefix():
     check(x, chunk=192, what="batch varlen")
 
 
+@pytest.mark.parametrize("batch", [40, 70])
+def test_many_requests(batch):
+    # up to 64 requests the split kernel lists the real work items and spreads
+    # them over the XCDs; past that it walks the padded item grid
+    rng = np.random.default_rng(30 + batch)
+    lens = [int(v) for v in rng.integers(0, 400, batch)]
+    parents = [gen.random_tree(int(n), rng) for n in rng.integers(1, 10, batch)]
+    x = small(lens, parents, 2, seed=31 + batch)
+    check(x, chunk=128, what=f"{batch} requests")
+
+
 def test_no_prefix_at_all():
     rng = np.random.default_rng(4)
     x = small([0, 0], [gen.random_tree(7, rng), gen.random_tree(3, rng)], 4, seed=14)
@@ -88,12 +99,12 @@ def test_sharp_scores_move_the_reference():
     check(x, chunk=1024, what="sharp scores")
 
 
-@pytest.mark.parametrize("chunk", [2048, 64])
+@pytest.mark.parametrize("chunk", [2048, 32])
 def test_reference_jump_mid_chunk(chunk):
     # one prefix key deep inside a chunk gets a score far above everything
     # before it, so the running reference max has to move mid-chunk; with
-    # 64-key chunks the key sits in chunk 23 of 32, past the merge's first
-    # batch of 16 partials, so the merge's running max moves too
+    # 32-key chunks the key sits in chunk 46 of 63, past the merge's first
+    # batch of 32 partials, so the merge's running max moves too
     rng = np.random.default_rng(7)
     x = small([2000], [gen.random_tree(5, rng)], 2, seed=19)
     key = 1500
