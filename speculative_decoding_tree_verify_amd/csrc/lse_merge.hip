@@ -22,8 +22,10 @@ namespace vamla {
 namespace {
 
 constexpr int kGroups = 4;          // float4 column groups per workgroup
-constexpr int kMaxMergeUnroll = 32; // chunks whose loads are issued together
 
+// kBatch = chunks whose loads are issued together (16 or 32; fewer registers
+// when the plan has at most 16 chunks)
+template <int kBatch>
 __global__ __launch_bounds__(kRowTile * kGroups) void lse_merge_kernel(MergeArgs a) {
   const int item = blockIdx.x;
   const int b = item / a.row_tiles;
@@ -49,11 +51,11 @@ __global__ __launch_bounds__(kRowTile * kGroups) void lse_merge_kernel(MergeArgs
   float m = -INFINITY;
   float sum = 0.f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int s0 = 0; s0 < S; s0 += kMaxMergeUnroll) {
-    float4 v[kMaxMergeUnroll];
-    float w[kMaxMergeUnroll];
+  for (int s0 = 0; s0 < S; s0 += kBatch) {
+    float4 v[kBatch];
+    float w[kBatch];
 #pragma unroll
-    for (int j = 0; j < kMaxMergeUnroll; ++j) {
+    for (int j = 0; j < kBatch; ++j) {
       if (s0 + j < S) {
         v[j] = o_p[(size_t)(s0 + j) * o_stride];
         w[j] = lse_p[(s0 + j) * kRowTile];
@@ -61,7 +63,7 @@ __global__ __launch_bounds__(kRowTile * kGroups) void lse_merge_kernel(MergeArgs
     }
     float mb = m;
 #pragma unroll
-    for (int j = 0; j < kMaxMergeUnroll; ++j)
+    for (int j = 0; j < kBatch; ++j)
       if (s0 + j < S) mb = fmaxf(mb, w[j]);
     if (mb > m) {                    // rescale what earlier batches summed
       const float c = __expf(m - mb);
@@ -73,7 +75,7 @@ __global__ __launch_bounds__(kRowTile * kGroups) void lse_merge_kernel(MergeArgs
       m = mb;
     }
 #pragma unroll
-    for (int j = 0; j < kMaxMergeUnroll; ++j) {
+    for (int j = 0; j < kBatch; ++j) {
       if (s0 + j < S) {
         const float e = __expf(w[j] - m);
         sum += e;
@@ -99,8 +101,11 @@ __global__ __launch_bounds__(kRowTile * kGroups) void lse_merge_kernel(MergeArgs
 }  // namespace
 
 hipError_t launch_lse_merge(const MergeArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL(lse_merge_kernel, dim3(a.batch * a.row_tiles, kD4 / kGroups), dim3(kRowTile * kGroups), 0,
-                     stream, a);
+  const dim3 grid(a.batch * a.row_tiles, kD4 / kGroups), block(kRowTile * kGroups);
+  if (a.max_chunks <= 16)
+    hipLaunchKernelGGL(lse_merge_kernel<16>, grid, block, 0, stream, a);
+  else
+    hipLaunchKernelGGL(lse_merge_kernel<32>, grid, block, 0, stream, a);
   return hipGetLastError();
 }
 
