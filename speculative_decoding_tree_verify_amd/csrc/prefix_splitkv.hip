@@ -43,10 +43,12 @@
 // lgkmcnt waits counted by hand, so that the V reads of the next tile stay in
 // flight under the current tile's MFMAs.  A 4-slot ring of 36 KB tiles (32 keys):
 //   latent: key k at k*1024, 16-byte piece c at slot c ^ g(k),
-//           g(k) = ((k & 3) << 2) | ((k >> 2) & 3)
-//   rope:   key k at 32 KB + k*128, piece c at slot c ^ ((k >> 1) & 7)
-// keeps the QK ds_read_b128 pattern (16 lanes per LDS cycle) and the PV
-// ds_read_b64_tr_b16 pattern (32 lanes per cycle) free of bank conflicts.
+//           g(k) = ((k & 3) << 2) | ((k >> 1) & 3)
+//   rope:   key k at 32 KB + k*128, piece c at slot c ^ (k & 7)
+// keeps the QK ds_read_b128 pattern (8 lanes, 128 bytes per LDS cycle: the
+// low three bits of g are distinct over 8 consecutive keys) and the PV
+// ds_read_b64_tr_b16 pattern (32 lanes, 256 bytes per cycle: bits 2-3 of g
+// distinct over 4 consecutive keys) free of bank conflicts.
 //
 // Softmax reference: each row keeps a reference m (log2 units) instead of a
 // running max, so the accumulators are never rescaled.  The first tile sets m
@@ -79,27 +81,12 @@ constexpr int kRing = 4;                      // tiles staged in LDS
 constexpr int kQSteps = kDqk / 32;            // 18 steps of v_mfma_f32_16x16x32_bf16
 constexpr int kPreQK = 4;                     // K fragments read ahead
 constexpr int kRsrcWord3 = 0x00020000;
-constexpr int kMaxTreeTiles = (kMaxTree + kKT - 1) / kKT;   // 3
 constexpr int kCompactBatch = 64;             // requests scanned per workgroup to list real items
 
-__device__ __forceinline__ int swz_latent(int k) { return ((k & 3) << 2) | ((k >> 2) & 3); }
-__device__ __forceinline__ int swz_rope(int k) { return (k >> 1) & 7; }
+__device__ __forceinline__ int swz_latent(int k) { return ((k & 3) << 2) | ((k >> 1) & 3); }
+__device__ __forceinline__ int swz_rope(int k) { return k & 7; }
 
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-
-__device__ __forceinline__ int xor_at_use(int base, int c) {
-  if (c == 0) return base;
-  int r;
-  asm volatile("v_xor_b32 %0, %2, %1" : "=v"(r) : "v"(base), "i"(c));
-  return r;
-}
-
-__device__ __forceinline__ bf16x8 tr_pair(const uint8_t* base, int off1, int off2) {
-  i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + off1));
-  i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + off2));
-  i16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-  return __builtin_bit_cast(bf16x8, v);
-}
 
 __device__ __forceinline__ void dma16_global(const void* src, uint32_t lds_addr) {
   uint32_t saved;
@@ -190,27 +177,13 @@ __device__ __forceinline__ void swap32(float& p, float& q) {
 __device__ __forceinline__ void swap16(float& p, float& q) {
   asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(p), "+v"(q));
 }
-// max / sum of x over the four lanes l % 16 == const
-__device__ __forceinline__ float max4(float x) {
-  float p = x, q = x;
-  swap16(p, q);
-  float y = vmax(p, q);
-  p = y;
-  q = y;
-  swap32(p, q);
-  return vmax(p, q);
-}
+// sum of x over the four lanes l % 16 == const
 __device__ __forceinline__ float sum4(float x) {
   float p = x, q = x;
   swap16(p, q);
   float y = p + q;
   p = y;
   q = y;
-  swap32(p, q);
-  return p + q;
-}
-__device__ __forceinline__ float sum_xor32(float x) {
-  float p = x, q = x;
   swap32(p, q);
   return p + q;
 }
@@ -250,7 +223,8 @@ __global__ __launch_bounds__(512, 1) void prefix_splitkv_kernel(PrefixArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t tile2[kTileLds];
   __shared__ __attribute__((aligned(1024))) uint8_t tile3[kTileLds];
   __shared__ __attribute__((aligned(16))) Shared sh;
-  auto ring = [&](int i) -> uint8_t* { i &= 3; return i == 0 ? tile0 : i == 1 ? tile1 : i == 2 ? tile2 : tile3; };
+  static_assert(kRing == 4, "ring slots are picked by the low two bits of the tile index");
+  auto ring = [&](int i) -> uint8_t* { i &= kRing - 1; return i == 0 ? tile0 : i == 1 ? tile1 : i == 2 ? tile2 : tile3; };
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
