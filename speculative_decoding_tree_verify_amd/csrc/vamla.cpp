@@ -66,11 +66,13 @@ int64_t choose_chunk(const vamla_params* p, int64_t row_tiles) {
   // Candidates: the longest prefix split into k chunks, k = 1, 2, ...; cost =
   // rounds of work items over the CUs times the keys the largest item
   // streams, plus the partials' traffic (which makes small problems prefer
-  // fewer, longer chunks).
+  // fewer, longer chunks).  The cost depends on the chunk size c(k) only, so
+  // the loop visits each distinct c once: after c, the next smaller size
+  // needs ceil(maxL / k) <= c - tile, i.e. k >= ceil(maxL / (c - tile)).
   int64_t best_c = VAMLA_KEY_TILE, best_cost = INT64_MAX;
   const int64_t kmax = std::min<int64_t>(ceil_div(maxL, VAMLA_KEY_TILE), 8192);
-  for (int64_t k = 1; k <= kmax; ++k) {
-    const int64_t c = ceil_div(ceil_div(maxL, k), VAMLA_KEY_TILE) * VAMLA_KEY_TILE;
+  for (int64_t k = 1, c = 0; k <= kmax; k = (c > VAMLA_KEY_TILE) ? ceil_div(maxL, c - VAMLA_KEY_TILE) : kmax + 1) {
+    c = ceil_div(ceil_div(maxL, k), VAMLA_KEY_TILE) * VAMLA_KEY_TILE;
     // each request contributes its full chunks plus at most one partial one
     const int64_t chunks =
         std::min<int64_t>(ceil_div(total, c) + (p->batch - 1), (int64_t)p->batch * ceil_div(maxL, c));

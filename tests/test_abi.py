@@ -86,6 +86,38 @@ def test_plan_fills_the_chip_for_the_64k_config(L):
     assert math.ceil(last / 32) * 32 + 96 <= info.chunk
 
 
+def _chunk_by_exhaustive_rule(p):
+    """The chunk-size rule of the planner, evaluated over every k (the longest
+    prefix split into k chunks), with the planner's cost constants."""
+    cus, overhead, partial, tile = 256, 256, 2, 32
+    maxL = p.max_prefix
+    if maxL <= tile:
+        return tile
+    total = p.total_prefix if p.total_prefix > 0 else maxL
+    row_tiles = -(-p.max_tree * p.num_heads // 64)
+    tree_keys = -(-p.max_tree // tile) * tile
+    best_c, best_cost = tile, None
+    for k in range(1, min(-(-maxL // tile), 8192) + 1):
+        c = -(-(-(-maxL // k)) // tile) * tile
+        chunks = min(-(-total // c) + p.batch - 1, p.batch * -(-maxL // c))
+        items = row_tiles * chunks
+        last = maxL - (-(-maxL // c) - 1) * c
+        cost = -(-items // cus) * (max(c, -(-last // tile) * tile + tree_keys) + overhead) + items * partial
+        if best_cost is None or cost < best_cost or (cost == best_cost and c > best_c):
+            best_c, best_cost = c, cost
+    return best_c
+
+
+@pytest.mark.parametrize("batch,heads,max_tree,max_prefix,total_prefix", [
+    (1, 16, 65, 65536, 65536), (1, 128, 65, 131072, 131072), (8, 16, 33, 185000, 8 * 47500),
+    (1, 16, 65, 4096, 4096), (64, 16, 65, 8192, 64 * 8192), (3, 16, 65, 100, 250), (1, 16, 1, 33, 33),
+    (2, 128, 65, 1000003, 1500000), (5, 64, 17, 77777, 200000), (1, 16, 65, 300000, 300000),
+])
+def test_plan_chunk_matches_the_exhaustive_rule(L, batch, heads, max_tree, max_prefix, total_prefix):
+    p = vb.Problem(batch, heads, 1 << 22, gen.SOFTMAX_SCALE, max_tree, max_tree * batch, max_prefix, total_prefix)
+    assert vb.plan(p).chunk == _chunk_by_exhaustive_rule(p)
+
+
 def test_explicit_chunk_is_kept(L):
     p = prob(2)
     p.chunk = 512
