@@ -209,6 +209,9 @@ def main():
     ap.add_argument("--config", type=int, default=3)
     ap.add_argument("--slot-mode", default=None, choices=["scrambled", "contiguous", "churned"],
                     help="slot layout of the pool (default: the workload's own)")
+    ap.add_argument("--launch", default="eager", choices=["eager", "graph"],
+                    help="eager: one library call per step; graph: each step replays a captured HIP graph "
+                         "of that call (one per pool copy)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 512 MiB device copy (counter calibration under rocprofv3 --pmc)")
@@ -227,7 +230,8 @@ def main():
 
     t0 = time.perf_counter()
     x = gen.config_inputs(args.config, slot_mode=args.slot_mode)
-    wname = workload_name(args.config) + (f", {args.slot_mode} slots" if args.slot_mode else "")
+    wname = workload_name(args.config) + (f", {args.slot_mode} slots" if args.slot_mode else "") + \
+        (", graph replay" if args.launch == "graph" else "")
     err(f"[bench] workload: {wname}  (inputs generated in {time.perf_counter() - t0:.1f} s)")
     alg = algorithmic(x)
     prob = vb.Problem.from_host(x.cu_prefix, x.cu_tree, x.num_heads, x.pool.shape[0], x.scale)
@@ -251,8 +255,29 @@ def main():
     lse = torch.empty((x.total_tree, x.num_heads), dtype=torch.float32, device=dev)
     err(f"[bench] {n_copies} pool copies of {pool_bytes / 1e6:.1f} MB rotated between steps")
 
-    def step(i):
+    def eager_step(i):
         vb.verify_attn_mla(prob, q, pools[i % n_copies], pre, tre, par, cup, cut, ws=ws, out=out, lse=lse)
+
+    step = eager_step
+    if args.launch == "graph":
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for i in range(n_copies):
+                eager_step(i)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graphs = []
+        for i in range(n_copies):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                eager_step(i)
+            graphs.append(g)
+        torch.cuda.synchronize()
+
+        def step(i):
+            graphs[i % n_copies].replay()
+        err(f"[bench] launch: {n_copies} captured graph(s), one verify step each")
 
     def split_only(i):
         vb.split_partials(prob, q, pools[i % n_copies], pre, tre, par, cup, cut, ws)
@@ -309,6 +334,8 @@ def main():
     cpu = None
     if not args.no_cpu:
         del pools
+        if args.launch == "graph":
+            del graphs, step
         cpu = cpu_baseline(x, alg["kv_bytes"])
         err(f"[bench] cpu oracle: {cpu['ms_per_step']:.1f} ms/step on {cpu['cores']} threads")
 
