@@ -91,9 +91,10 @@ typedef struct vamla_params {
   int64_t pool_slots;       /* P >= 1: rows in kv_pool */
   float softmax_scale;      /* sigma > 0 (finite), applied to q.k before the exponential */
   int32_t max_tree;         /* >= every N_b, in [1, 65] (planning bound) */
-  int32_t total_tree;       /* T = cu_tree[B] >= 1 */
+  int32_t total_tree;       /* T = cu_tree[B] >= 1; with B = 1 the kernels take the request's
+                               bounds from total_tree / total_prefix and do not read cu_* */
   int64_t max_prefix;       /* >= every L_b (planning bound), >= 0 */
-  int64_t total_prefix;     /* cu_prefix[B]; used to choose the chunk size */
+  int64_t total_prefix;     /* cu_prefix[B]; chooses the chunk size (and is L when B = 1) */
   int32_t chunk;            /* prefix keys per split; multiple of 32, or 0 = choose automatically */
   uint32_t flags;           /* reserved, must be 0 */
   const int32_t* cu_prefix; /* device [B+1], cu_prefix[0] = 0, non-decreasing */

@@ -34,6 +34,8 @@ struct PrefixArgs {
   int32_t max_chunks;
   int32_t batch;
   int32_t grid_items;         // multiple of 8
+  int32_t total_prefix;       // = cu_prefix[B]; with B = 1 the kernel takes
+  int32_t total_tree;         // the request's bounds from these two, not cu_*
   float scale_log2;           // softmax_scale * log2(e)
 };
 
@@ -50,6 +52,8 @@ struct MergeArgs {
   int32_t row_tiles;
   int32_t max_chunks;
   int32_t batch;
+  int32_t total_prefix;       // as in PrefixArgs
+  int32_t total_tree;
 };
 
 hipError_t launch_prefix_splitkv(const PrefixArgs& a, hipStream_t stream);

@@ -30,13 +30,15 @@ __global__ __launch_bounds__(kRowTile * kGroups) void lse_merge_kernel(MergeArgs
   const int item = blockIdx.x;
   const int b = item / a.row_tiles;
   const int tile = item - b * a.row_tiles;
-  const int t0 = a.cu_tree[b];
-  const int rows_b = (a.cu_tree[b + 1] - t0) * a.num_heads;
+  // a single request's bounds are the call's totals (no load before the partials')
+  const bool one = a.batch == 1;
+  const int t0 = one ? 0 : a.cu_tree[b];
+  const int rows_b = ((one ? a.total_tree : a.cu_tree[b + 1]) - t0) * a.num_heads;
   const int rit = threadIdx.x & (kRowTile - 1);
   const int d4 = blockIdx.y * kGroups + (threadIdx.x >> 6);
   const int r = tile * kRowTile + rit;
   if (r >= rows_b) return;
-  const int L = a.cu_prefix[b + 1] - a.cu_prefix[b];
+  const int L = one ? a.total_prefix : a.cu_prefix[b + 1] - a.cu_prefix[b];
   // a prefix longer than max_prefix is a caller error; never read past the plan
   const int S = max(1, min((L + a.chunk - 1) / a.chunk, a.max_chunks));
 

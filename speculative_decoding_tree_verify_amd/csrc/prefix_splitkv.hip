@@ -239,11 +239,17 @@ __global__ __launch_bounds__(512, 1) void prefix_splitkv_kernel(PrefixArgs a) {
   // would cost more than it saves, and the padded grid is used as it is.
   int b, s, tile;
   const int chunk = a.chunk, max_chunks = a.max_chunks;
+  // A single request's bounds are the call's totals: nothing is loaded
+  // before the first tile's slot indices.
+  const bool one = a.batch == 1;
+  const int one_L = a.total_prefix, one_N = a.total_tree;
+  auto len_p = [&](int i) -> int { return one ? one_L : a.cu_prefix[i + 1] - a.cu_prefix[i]; };
+  auto len_t = [&](int i) -> int { return one ? one_N : a.cu_tree[i + 1] - a.cu_tree[i]; };
   auto nch_of = [&](int L) { return max(1, min((L + chunk - 1) / chunk, max_chunks)); };
   if (a.batch <= kCompactBatch) {
     auto items_of = [&](int i) {
-      const int L_i = a.cu_prefix[i + 1] - a.cu_prefix[i];
-      const int rt = min((( a.cu_tree[i + 1] - a.cu_tree[i]) * a.num_heads + kRowTile - 1) / kRowTile, a.row_tiles);
+      const int L_i = len_p(i);
+      const int rt = min((len_t(i) * a.num_heads + kRowTile - 1) / kRowTile, a.row_tiles);
       return __builtin_amdgcn_readfirstlane(nch_of(L_i) * max(rt, 0));
     };
     int total = 0;
@@ -259,7 +265,7 @@ __global__ __launch_bounds__(512, 1) void prefix_splitkv_kernel(PrefixArgs a) {
       r -= n;
       ++b;
     }
-    const int rt_b = min(((a.cu_tree[b + 1] - a.cu_tree[b]) * a.num_heads + kRowTile - 1) / kRowTile, a.row_tiles);
+    const int rt_b = min((len_t(b) * a.num_heads + kRowTile - 1) / kRowTile, a.row_tiles);
     s = r / rt_b;
     tile = r - s * rt_b;
   } else {
@@ -272,14 +278,14 @@ __global__ __launch_bounds__(512, 1) void prefix_splitkv_kernel(PrefixArgs a) {
     s = rem / a.row_tiles;
     tile = rem - s * a.row_tiles;
   }
-  const int p0 = a.cu_prefix[b];
-  const int L = a.cu_prefix[b + 1] - p0;
+  const int p0 = one ? 0 : a.cu_prefix[b];
+  const int L = len_p(b);
   const int nchunks = nch_of(L);
   if (s >= nchunks) return;
   const int kbeg = s * chunk;
   const int kend = min(kbeg + chunk, L);
-  const int t0 = a.cu_tree[b];
-  const int n_b = a.cu_tree[b + 1] - t0;
+  const int t0 = one ? 0 : a.cu_tree[b];
+  const int n_b = len_t(b);
   const int rows_b = n_b * a.num_heads;
   if (tile * kRowTile >= rows_b) return;
   const int n_tree = min(n_b, kMaxTree);
@@ -287,6 +293,23 @@ __global__ __launch_bounds__(512, 1) void prefix_splitkv_kernel(PrefixArgs a) {
   const int ntt = s == nchunks - 1 ? (n_tree + kKT - 1) / kKT : 0;
   const int ntiles = ntp + ntt;
   const int nfull = (kend - kbeg) / kKT;           // prefix tiles with all 32 keys
+
+  // slot index of key 8c + (lane >> 3) of tile t, for PV wave c
+  auto slot_ptr = [&](int t, int c) -> const int* {
+    t = min(t, ntiles - 1);
+    const bool tree = t >= ntp;
+    const int* list = tree ? a.tree_slot + t0 : a.prefix_slot + p0;
+    const int base = tree ? (t - ntp) * kKT : kbeg + t * kKT;
+    const int last = tree ? n_tree - 1 : kend - 1;
+    return list + min(base + 8 * c + (lane >> 3), last);
+  };
+  // The PV waves read the slot indices of tiles 0..3 before the tree masks
+  // are built, so their round trip overlaps that of the parent array.
+  uint32_t slot_first[4] = {0u, 0u, 0u, 0u};
+  if (!is_qk) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) slot_first[t] = (uint32_t)*slot_ptr(t, w - 4);
+  }
 
   if (ntt > 0) {
     for (int i = threadIdx.x; i < n_tree; i += blockDim.x) sh.par[i] = a.parent[t0 + i];
@@ -496,15 +519,8 @@ __global__ __launch_bounds__(512, 1) void prefix_splitkv_kernel(PrefixArgs a) {
       pvb[hi] = (key * 1024 + 256 * c + 8 * (s2 & 1)) | (((2 * (bb & 1) + (s2 >> 1)) ^ swz_latent(key)) << 4);
     }
   }
-  // slot of key 8c + (lane >> 3) of tile t; valid after the next vmcnt wait
-  auto load_slot = [&](int t) -> uint32_t {
-    t = min(t, ntiles - 1);
-    const bool tree = t >= ntp;
-    const int* list = tree ? a.tree_slot + t0 : a.prefix_slot + p0;
-    const int base = tree ? (t - ntp) * kKT : kbeg + t * kKT;
-    const int last = tree ? n_tree - 1 : kend - 1;
-    return load_u32_async(list + min(base + 8 * c + (lane >> 3), last));
-  };
+  // slots of tile t; valid after the next vmcnt wait
+  auto load_slot = [&](int t) -> uint32_t { return load_u32_async(slot_ptr(t, c)); };
   for (;;) {
     // Slot ring: svd holds the slots of tile it+2 (gathered in iteration it),
     // svn those of tile it+3.  Each iteration loads the next slots before its
@@ -512,10 +528,9 @@ __global__ __launch_bounds__(512, 1) void prefix_splitkv_kernel(PrefixArgs a) {
     // wait for a gather.
     uint32_t svd, svn;
     {
-      uint32_t s0 = load_slot(0), s1 = load_slot(1);
-      svd = load_slot(2);
-      svn = load_slot(3);
-      asm volatile("s_waitcnt vmcnt(0)" : "+v"(s0), "+v"(s1), "+v"(svd), "+v"(svn) :: "memory");
+      const uint32_t s0 = slot_first[0], s1 = slot_first[1];
+      svd = slot_first[2];
+      svn = slot_first[3];
 #pragma unroll
       for (int d = 0; d < 9; ++d) gather_one(a.pool, s0, tile0, c, lane, d);
       if (ntiles > 1) {

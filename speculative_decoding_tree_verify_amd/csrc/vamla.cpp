@@ -159,6 +159,8 @@ int split_launch(const vamla_params* p, const vamla_plan_info& pl, const uint16_
   a.max_chunks = pl.max_chunks;
   a.batch = p->batch;
   a.grid_items = pl.grid_items;
+  a.total_prefix = (int32_t)p->total_prefix;
+  a.total_tree = p->total_tree;
   a.scale_log2 = p->softmax_scale * 1.4426950408889634f;
   return launch_prefix_splitkv(a, stream) == hipSuccess ? VAMLA_OK : VAMLA_ERR_LAUNCH;
 }
@@ -176,6 +178,8 @@ int merge_launch(const vamla_params* p, const vamla_plan_info& pl, uint16_t* out
   a.row_tiles = pl.row_tiles;
   a.max_chunks = pl.max_chunks;
   a.batch = p->batch;
+  a.total_prefix = (int32_t)p->total_prefix;
+  a.total_tree = p->total_tree;
   return launch_lse_merge(a, stream) == hipSuccess ? VAMLA_OK : VAMLA_ERR_LAUNCH;
 }
 
