@@ -73,9 +73,11 @@ int64_t choose_chunk(const vamla_params* p, int64_t row_tiles) {
   const int64_t kmax = std::min<int64_t>(ceil_div(maxL, VAMLA_KEY_TILE), 8192);
   for (int64_t k = 1, c = 0; k <= kmax; k = (c > VAMLA_KEY_TILE) ? ceil_div(maxL, c - VAMLA_KEY_TILE) : kmax + 1) {
     c = ceil_div(ceil_div(maxL, k), VAMLA_KEY_TILE) * VAMLA_KEY_TILE;
-    // each request contributes its full chunks plus at most one partial one
+    // each request contributes its full chunks plus at most one partial one;
+    // only the lengths' sum and maximum are known here, and a request's
+    // last chunk is half full on average, so the partial ones add about B/2
     const int64_t chunks =
-        std::min<int64_t>(ceil_div(total, c) + (p->batch - 1), (int64_t)p->batch * ceil_div(maxL, c));
+        std::min<int64_t>(ceil_div(total, c) + ceil_div(p->batch - 1, 2), (int64_t)p->batch * ceil_div(maxL, c));
     const int64_t items = row_tiles * chunks;
     const int64_t rounds = ceil_div(items, kCUs);
     const int64_t last = maxL - (ceil_div(maxL, c) - 1) * c;

@@ -99,7 +99,7 @@ def _chunk_by_exhaustive_rule(p):
     best_c, best_cost = tile, None
     for k in range(1, min(-(-maxL // tile), 8192) + 1):
         c = -(-(-(-maxL // k)) // tile) * tile
-        chunks = min(-(-total // c) + p.batch - 1, p.batch * -(-maxL // c))
+        chunks = min(-(-total // c) + -(-(p.batch - 1) // 2), p.batch * -(-maxL // c))
         items = row_tiles * chunks
         last = maxL - (-(-maxL // c) - 1) * c
         cost = -(-items // cus) * (max(c, -(-last // tile) * tile + tree_keys) + overhead) + items * partial

@@ -72,6 +72,27 @@ def test_many_requests(batch):
     check(x, chunk=128, what=f"{batch} requests")
 
 
+def test_single_request_bounds_match_the_batched_path():
+    # one request takes its bounds from the call's totals, a batch reads
+    # cu_prefix / cu_tree: with the same chunk the request's partials and
+    # merge are the same arithmetic, so its rows must agree bit for bit
+    rng = np.random.default_rng(8)
+    par_a, par_b = gen.random_tree(9, rng), gen.random_tree(5, rng)
+    both = small([900, 333], [par_a, par_b], 4, seed=20)
+    check(both, chunk=128, what="two requests")
+    one = gen.VerifyInputs(q=both.q[:9].copy(), pool=both.pool, prefix_slot_idx=both.prefix_slot_idx[:900].copy(),
+                           tree_slot_idx=both.tree_slot_idx[:9].copy(), parent=both.parent[:9].copy(),
+                           cu_prefix=np.array([0, 900], np.int32), cu_tree=np.array([0, 9], np.int32),
+                           num_heads=both.num_heads, scale=both.scale)
+    out1, lse1, _ = run_verify(one, 128)
+    out2, lse2, _ = run_verify(both, 128)
+    assert np.array_equal(lse1, lse2[:9])          # fp32 values, widened exactly
+    assert np.array_equal(out1, out2[:9])          # bf16 values, widened exactly
+    ro, rl = oracle_full(one)
+    assert_close_lse(lse1, rl, "one request")
+    assert_close_out(out1, ro, "one request")
+
+
 def test_no_prefix_at_all():
     rng = np.random.default_rng(4)
     x = small([0, 0], [gen.random_tree(7, rng), gen.random_tree(3, rng)], 4, seed=14)
