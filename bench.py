@@ -15,7 +15,7 @@ Prints ONE JSON line (stdout):
   cpu_baseline the fp64 oracle on host cores, same workload (test infrastructure)
 Details go to stderr.
 
-  python bench.py [--steps K] [--warmup W] [--config 1..5] [--no-cpu]
+  python bench.py [--steps K] [--warmup W] [--config 1..7] [--no-cpu]
                   [--slot-mode scrambled|contiguous|churned]
 
 Besides the mean over the K timed steps, stderr and `config` carry per-step

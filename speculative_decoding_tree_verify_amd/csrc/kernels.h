@@ -54,6 +54,8 @@ struct MergeArgs {
   int32_t batch;
   int32_t total_prefix;       // as in PrefixArgs
   int32_t total_tree;
+  int32_t row_bits;           // log2 of the rows a wave covers (<= 6): live rows of a tile, rounded up
+  int32_t chunk_wave_bits;    // log2 of the waves that split one column group's chunks (<= 2)
 };
 
 hipError_t launch_prefix_splitkv(const PrefixArgs& a, hipStream_t stream);

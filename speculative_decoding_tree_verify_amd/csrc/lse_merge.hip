@@ -10,90 +10,147 @@
 // Phase 2; "The Architecture Detective: ...", "The Message in Full").
 // Chunks past a request's prefix were never written and are not read.
 //
-// Layout: partials are [item][128 d4][64 rows][4 floats].  A 256-thread
-// workgroup covers one row tile and four float4 column groups; thread =
-// (column group, row), so each wave reads one coalesced 1 KB piece per chunk.
-// Every thread keeps its chunks' loads in flight at once: the pass is a
-// stream over the partials and needs many waves per CU to reach HBM speed.
+// Layout: partials are [item][128 d4][64 rows][4 floats], so for one chunk
+// and one float4 column group the rows of a tile are 1 KB of contiguous
+// memory.  A 256-thread workgroup covers one row tile and 4 / CW column
+// groups, CW waves per column group (CW = 1, 2 or 4).  A wave's 64 lanes are
+// RL rows x CL chunk lanes (RL = the tile's live rows rounded up to a power
+// of two, at most 64; RL * CL = 64), so every load instruction reads CL
+// segments of RL * 16 >= 64 contiguous bytes.  Thread (chunk wave cw, chunk
+// lane c) takes chunks k, k + CW*CL, ... with k = cw * CL + c, folds them with
+// a running max (the loads of a batch in flight together), and the partial
+// states (max, sum, float4) are combined across chunk lanes by lane shuffles
+// and across the CW waves through LDS.  With few rows and many chunks
+// (decode-like calls) this keeps 128 workgroups per row tile busy instead of
+// a handful of lanes walking every chunk in turn; with many row tiles the
+// host takes CW = 1 and RL = 64, one wave per column group and no exchange.
 
 #include "kernels.h"
 
 namespace vamla {
 namespace {
 
-constexpr int kGroups = 4;          // float4 column groups per workgroup
+constexpr int kWaves = 4;
+constexpr int kBatch = 16;          // chunks whose loads a thread issues together
 
-// kBatch = chunks whose loads are issued together (16 or 32; fewer registers
-// when the plan has at most 16 chunks)
-template <int kBatch>
-__global__ __launch_bounds__(kRowTile * kGroups) void lse_merge_kernel(MergeArgs a) {
+struct State {
+  float m, s;
+  float4 a;
+};
+
+__device__ __forceinline__ void fold(State& x, const State& y) {
+  const float M = fmaxf(x.m, y.m);
+  // an empty state (m = -inf) has weight 0; two empty states stay empty
+  const float cx = x.m == -INFINITY ? 0.f : __expf(x.m - M);
+  const float cy = y.m == -INFINITY ? 0.f : __expf(y.m - M);
+  x.s = x.s * cx + y.s * cy;
+  x.a.x = x.a.x * cx + y.a.x * cy;
+  x.a.y = x.a.y * cx + y.a.y * cy;
+  x.a.z = x.a.z * cx + y.a.z * cy;
+  x.a.w = x.a.w * cx + y.a.w * cy;
+  x.m = M;
+}
+
+__device__ __forceinline__ State shfl_state(const State& x, int mask) {
+  State y;
+  y.m = __shfl_xor(x.m, mask);
+  y.s = __shfl_xor(x.s, mask);
+  y.a.x = __shfl_xor(x.a.x, mask);
+  y.a.y = __shfl_xor(x.a.y, mask);
+  y.a.z = __shfl_xor(x.a.z, mask);
+  y.a.w = __shfl_xor(x.a.w, mask);
+  return y;
+}
+
+__global__ __launch_bounds__(64 * kWaves) void lse_merge_kernel(MergeArgs a) {
+  __shared__ State red[kWaves][kRowTile];
   const int item = blockIdx.x;
   const int b = item / a.row_tiles;
   const int tile = item - b * a.row_tiles;
+  const int cw_bits = a.chunk_wave_bits;
+  const int CW = 1 << cw_bits;
   // a single request's bounds are the call's totals (no load before the partials')
   const bool one = a.batch == 1;
   const int t0 = one ? 0 : a.cu_tree[b];
   const int rows_b = ((one ? a.total_tree : a.cu_tree[b + 1]) - t0) * a.num_heads;
-  const int rit = threadIdx.x & (kRowTile - 1);
-  const int d4 = blockIdx.y * kGroups + (threadIdx.x >> 6);
-  const int r = tile * kRowTile + rit;
-  if (r >= rows_b) return;
+  if (tile * kRowTile >= rows_b) return;
   const int L = one ? a.total_prefix : a.cu_prefix[b + 1] - a.cu_prefix[b];
   // a prefix longer than max_prefix is a caller error; never read past the plan
   const int S = max(1, min((L + a.chunk - 1) / a.chunk, a.max_chunks));
+
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int rl_bits = a.row_bits;
+  const int RL = 1 << rl_bits;
+  const int CL = 64 >> rl_bits;
+  const int rit = lane & (RL - 1);                // row within the tile
+  const int cl = lane >> rl_bits;                 // chunk lane
+  const int cw = w & (CW - 1);                    // chunk wave
+  const int d4 = blockIdx.y * (kWaves >> cw_bits) + (w >> cw_bits);
+  const int k0 = cw * CL + cl;
+  const int kstep = CW * CL;
+  const bool live = tile * kRowTile + rit < rows_b;
 
   const size_t p0 = ((size_t)b * a.row_tiles + tile) * a.max_chunks;
   const float* lse_p = a.part_lse + p0 * kRowTile + rit;
   const float4* o_p = (const float4*)a.part_o + (p0 * kD4 + d4) * kRowTile + rit;
   const size_t o_stride = (size_t)kD4 * kRowTile;          // float4s per chunk partial
 
-  // One round trip: the chunks' lse values and partials are loaded
-  // together, the max is taken from registers.  Requests with more chunks
-  // than fit in one batch fold their batches with a running max.
-  float m = -INFINITY;
-  float sum = 0.f;
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int s0 = 0; s0 < S; s0 += kBatch) {
-    float4 v[kBatch];
-    float w[kBatch];
+  State st{-INFINITY, 0.f, make_float4(0.f, 0.f, 0.f, 0.f)};
+  if (live) {
+    for (int s0 = k0; s0 < S; s0 += kBatch * kstep) {
+      float4 v[kBatch];
+      float lw[kBatch];
 #pragma unroll
-    for (int j = 0; j < kBatch; ++j) {
-      if (s0 + j < S) {
-        v[j] = o_p[(size_t)(s0 + j) * o_stride];
-        w[j] = lse_p[(s0 + j) * kRowTile];
+      for (int j = 0; j < kBatch; ++j) {
+        const int s = s0 + j * kstep;
+        if (s < S) {
+          v[j] = o_p[(size_t)s * o_stride];
+          lw[j] = lse_p[s * kRowTile];
+        }
       }
-    }
-    float mb = m;
+      float mb = st.m;
 #pragma unroll
-    for (int j = 0; j < kBatch; ++j)
-      if (s0 + j < S) mb = fmaxf(mb, w[j]);
-    if (mb > m) {                    // rescale what earlier batches summed
-      const float c = __expf(m - mb);
-      sum *= c;
-      acc.x *= c;
-      acc.y *= c;
-      acc.z *= c;
-      acc.w *= c;
-      m = mb;
-    }
+      for (int j = 0; j < kBatch; ++j)
+        if (s0 + j * kstep < S) mb = fmaxf(mb, lw[j]);
+      if (mb > st.m) {                 // rescale what earlier batches summed
+        const float c = __expf(st.m - mb);
+        st.s *= c;
+        st.a.x *= c;
+        st.a.y *= c;
+        st.a.z *= c;
+        st.a.w *= c;
+        st.m = mb;
+      }
 #pragma unroll
-    for (int j = 0; j < kBatch; ++j) {
-      if (s0 + j < S) {
-        const float e = __expf(w[j] - m);
-        sum += e;
-        acc.x = fmaf(e, v[j].x, acc.x);
-        acc.y = fmaf(e, v[j].y, acc.y);
-        acc.z = fmaf(e, v[j].z, acc.z);
-        acc.w = fmaf(e, v[j].w, acc.w);
+      for (int j = 0; j < kBatch; ++j) {
+        if (s0 + j * kstep < S) {
+          const float e = __expf(lw[j] - st.m);
+          st.s += e;
+          st.a.x = fmaf(e, v[j].x, st.a.x);
+          st.a.y = fmaf(e, v[j].y, st.a.y);
+          st.a.z = fmaf(e, v[j].z, st.a.z);
+          st.a.w = fmaf(e, v[j].w, st.a.w);
+        }
       }
     }
   }
-  const float inv = 1.f / sum;
-  const size_t orow = (size_t)t0 * a.num_heads + r;   // global row (t, h)
-  if (d4 == 0) a.lse[orow] = m + logf(sum);
+  // chunk lanes of a row: lanes rit + RL * c, c = 0 .. CL-1
+  for (int mask = RL; mask < 64; mask <<= 1) fold(st, shfl_state(st, mask));
+  if (CW > 1) {
+    if (cl == 0) red[w][rit] = st;
+    __syncthreads();
+    for (int i = 1; i < CW; ++i)
+      if (cw == 0) fold(st, red[w + i][rit]);
+  }
+  if (cw != 0 || cl != 0 || !live) return;
+
+  const float inv = 1.f / st.s;
+  const size_t orow = (size_t)t0 * a.num_heads + tile * kRowTile + rit;   // global row (t, h)
+  if (d4 == 0) a.lse[orow] = st.m + logf(st.s);
   // bf16, round to nearest even
-  const __bf16 h0 = (__bf16)(acc.x * inv), h1 = (__bf16)(acc.y * inv), h2 = (__bf16)(acc.z * inv),
-               h3 = (__bf16)(acc.w * inv);
+  const __bf16 h0 = (__bf16)(st.a.x * inv), h1 = (__bf16)(st.a.y * inv), h2 = (__bf16)(st.a.z * inv),
+               h3 = (__bf16)(st.a.w * inv);
   uint2 pk;
   pk.x = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
   pk.y = (uint32_t)__builtin_bit_cast(uint16_t, h2) | ((uint32_t)__builtin_bit_cast(uint16_t, h3) << 16);
@@ -103,11 +160,9 @@ __global__ __launch_bounds__(kRowTile * kGroups) void lse_merge_kernel(MergeArgs
 }  // namespace
 
 hipError_t launch_lse_merge(const MergeArgs& a, hipStream_t stream) {
-  const dim3 grid(a.batch * a.row_tiles, kD4 / kGroups), block(kRowTile * kGroups);
-  if (a.max_chunks <= 16)
-    hipLaunchKernelGGL(lse_merge_kernel<16>, grid, block, 0, stream, a);
-  else
-    hipLaunchKernelGGL(lse_merge_kernel<32>, grid, block, 0, stream, a);
+  if (a.row_bits < 0 || a.row_bits > 6 || a.chunk_wave_bits < 0 || a.chunk_wave_bits > 2) return hipErrorInvalidValue;
+  const dim3 grid(a.batch * a.row_tiles, (kD4 / kWaves) << a.chunk_wave_bits), block(64 * kWaves);
+  hipLaunchKernelGGL(lse_merge_kernel, grid, block, 0, stream, a);
   return hipGetLastError();
 }
 

@@ -335,6 +335,11 @@ __global__ __launch_bounds__(512, 1) void prefix_splitkv_kernel(PrefixArgs a) {
   const size_t pidx = ((size_t)b * a.row_tiles + tile) * a.max_chunks + s;
   if (is_qk) {
     const int pr = w >> 1, hf = w & 1, q4 = lane >> 4, l16 = lane & 15;
+    // 16-row halves of this pair that hold live query rows (0, 1 or 2): the
+    // MFMAs (and, with none live, the K reads) of dead halves are skipped;
+    // their scores stay 0, so their P is finite and their rows are dropped
+    const int live_pr = rows_b - tile * kRowTile - 32 * pr;
+    const int nb_live = __builtin_amdgcn_readfirstlane(live_pr <= 0 ? 0 : live_pr <= 16 ? 1 : 2);
     bf16x8 qf[kQSteps][2];
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
@@ -394,7 +399,7 @@ __global__ __launch_bounds__(512, 1) void prefix_splitkv_kernel(PrefixArgs a) {
         if (it >= 2) vote = *(const f32x4*)sh.want[it & 1];
         __builtin_amdgcn_sched_barrier(0);
         bf16x8 kf[kPreQK];
-        if (it < ntiles) {
+        if (it < ntiles && nb_live > 0) {
 #pragma unroll
           for (int i = 0; i < kPreQK; ++i) kf[i] = kfrag(i);
         }
@@ -429,13 +434,23 @@ __global__ __launch_bounds__(512, 1) void prefix_splitkv_kernel(PrefixArgs a) {
         }
         if (it < ntiles) {
           f32x4 sacc[2] = {f32x4{}, f32x4{}};
+          if (nb_live == 2) {
 #pragma unroll
-          for (int st = 0; st < kQSteps; ++st) {
-            const bf16x8 cur = kf[st % kPreQK];
-            if (st + kPreQK < kQSteps) kf[st % kPreQK] = kfrag(st + kPreQK);
-            sacc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur, qf[st][0], sacc[0], 0, 0, 0);
-            sacc[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur, qf[st][1], sacc[1], 0, 0, 0);
-            __builtin_amdgcn_sched_barrier(0);
+            for (int st = 0; st < kQSteps; ++st) {
+              const bf16x8 cur = kf[st % kPreQK];
+              if (st + kPreQK < kQSteps) kf[st % kPreQK] = kfrag(st + kPreQK);
+              sacc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur, qf[st][0], sacc[0], 0, 0, 0);
+              sacc[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur, qf[st][1], sacc[1], 0, 0, 0);
+              __builtin_amdgcn_sched_barrier(0);
+            }
+          } else if (nb_live == 1) {
+#pragma unroll
+            for (int st = 0; st < kQSteps; ++st) {
+              const bf16x8 cur = kf[st % kPreQK];
+              if (st + kPreQK < kQSteps) kf[st % kPreQK] = kfrag(st + kPreQK);
+              sacc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur, qf[st][0], sacc[0], 0, 0, 0);
+              __builtin_amdgcn_sched_barrier(0);
+            }
           }
           // lane holds keys 16hf + 4q4 + r (r = 0..3) of rows 32pr + 16nb + l16
           // masks only on the last prefix tile (ragged) and the tree tiles
@@ -506,6 +521,10 @@ __global__ __launch_bounds__(512, 1) void prefix_splitkv_kernel(PrefixArgs a) {
 
   // ---------------- PV waves ----------------
   const int c = w - 4;
+  // rows 32..63 of the tile: with none live their MFMAs are skipped (a
+  // uniform branch around each; the LDS reads, and so the hand-counted
+  // waits, stay as they are)
+  const bool rb1_live = __builtin_amdgcn_readfirstlane(rows_b - tile * kRowTile > 32 ? 1 : 0) != 0;
   f32x16 o[8];
 #pragma unroll
   for (int d = 0; d < 8; ++d) o[d] = f32x16{};
@@ -586,7 +605,8 @@ __global__ __launch_bounds__(512, 1) void prefix_splitkv_kernel(PrefixArgs a) {
           for (int rb = 0; rb < 2; ++rb) {
             const int j = 2 * ks + rb;
             if (cb == 0) wait_lgkm((3 - j) + 2 * f, pop[j]);
-            o[cb + 4 * rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[f], pop[j], o[cb + 4 * rb], 0, 0, 0);
+            if (rb == 0 || rb1_live)
+              o[cb + 4 * rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[f], pop[j], o[cb + 4 * rb], 0, 0, 0);
             if (rb == 1) vf[f] = vread(nslot, f);  // V(it-1); at it = ntiles+1 a harmless re-read
             __builtin_amdgcn_sched_barrier(0);
           }

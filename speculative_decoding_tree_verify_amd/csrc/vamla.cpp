@@ -182,6 +182,16 @@ int merge_launch(const vamla_params* p, const vamla_plan_info& pl, uint16_t* out
   a.batch = p->batch;
   a.total_prefix = (int32_t)p->total_prefix;
   a.total_tree = p->total_tree;
+  // a wave covers the live rows of a tile (at most max_tree * H when there is
+  // one row tile), its other lanes split the chunks
+  const int64_t tile_rows = std::min<int64_t>(kRowTile, (int64_t)p->max_tree * p->num_heads);
+  int bits = 0;
+  while ((1 << bits) < tile_rows) ++bits;
+  a.row_bits = bits;
+  // waves per column group that split its chunks: as few as keep >= 512
+  // workgroups (2 per CU) in the grid
+  const int64_t base = (int64_t)p->batch * pl.row_tiles * (kD4 / 4);
+  a.chunk_wave_bits = base >= 512 ? 0 : base >= 256 ? 1 : 2;
   return launch_lse_merge(a, stream) == hipSuccess ? VAMLA_OK : VAMLA_ERR_LAUNCH;
 }
 

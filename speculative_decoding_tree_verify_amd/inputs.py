@@ -274,12 +274,16 @@ CONFIG_NAMES = {
     3: "B=1 H=16 L=65536 N=65 depth-8 branching<=4 tree, 131072-slot scrambled pool",
     4: "B=1 H=128 L=131072 N=65 depth-8 tree, 2^20-slot churned pool",
     5: "B=8 H=16 L~logU[4096,185000] N=33 depth<=8 trees, shared 2^21-slot churned pool",
+    # small-rows regime (fewer query rows than the ~315 flop/byte ridge needs:
+    # the step is bound by reading KV from HBM)
+    6: "decode: B=1 H=16 L=131072 N=1 (root only), 262144-slot scrambled pool",
+    7: "B=1 H=16 L=185000 N=9 chain-of-8-plus-branch, 262144-slot scrambled pool",
 }
 
 
 def config_inputs(k: int, slot_mode: Optional[str] = None, std_q: float = 0.1,
                   poison_unused: bool = True) -> VerifyInputs:
-    """Inputs of workload configuration k (1..5); seeds derive from 1000*k."""
+    """Inputs of workload configuration k (1..7); seeds derive from 1000*k."""
     seed = 1000 * k
     tree_rng = np.random.default_rng(np.random.SeedSequence(seed + 7))
     if k == 1:
@@ -300,4 +304,10 @@ def config_inputs(k: int, slot_mode: Optional[str] = None, std_q: float = 0.1,
         trees = [bounded_tree(33, tree_rng) for _ in range(8)]
         return make_inputs(lens, trees, 16, 1 << 21, slot_mode or "churned", seed,
                            std_q=std_q, poison_unused=poison_unused)
+    if k == 6:
+        return make_inputs([131072], [np.array([-1], np.int32)], 16, 1 << 18,
+                           slot_mode or "scrambled", seed, std_q=std_q, poison_unused=poison_unused)
+    if k == 7:
+        return make_inputs([185000], [chain_plus_branch()], 16, 1 << 18,
+                           slot_mode or "scrambled", seed, std_q=std_q, poison_unused=poison_unused)
     raise ValueError(k)

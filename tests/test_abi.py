@@ -55,11 +55,13 @@ def prob(k):
         3: vb.Problem(1, 16, 131072, gen.SOFTMAX_SCALE, 65, 65, 65536, 65536),
         4: vb.Problem(1, 128, 1 << 20, gen.SOFTMAX_SCALE, 65, 65, 131072, 131072),
         5: vb.Problem(8, 16, 1 << 21, gen.SOFTMAX_SCALE, 33, 264, 185000, 8 * 47500),
+        6: vb.Problem(1, 16, 1 << 18, gen.SOFTMAX_SCALE, 1, 1, 131072, 131072),
+        7: vb.Problem(1, 16, 1 << 18, gen.SOFTMAX_SCALE, 9, 9, 185000, 185000),
     }
     return table[k]
 
 
-@pytest.mark.parametrize("k", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("k", [1, 2, 3, 4, 5, 6, 7])
 def test_plan_covers_the_problem(L, k):
     p = prob(k)
     info = vb.plan(p)

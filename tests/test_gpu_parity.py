@@ -54,6 +54,15 @@ def test_several_row_tiles():
     check(x, chunk=256, what="3 row tiles")
 
 
+@pytest.mark.parametrize("H,N", [(1, 9), (2, 9), (5, 9), (7, 9), (16, 1)])
+def test_partly_live_row_tile(H, N):
+    # 9, 18, 45, 63 and 16 live rows in the only row tile: the MFMAs of dead
+    # 16-row halves (QK) and of dead rows 32..63 (PV) are skipped
+    rng = np.random.default_rng(40 + H)
+    x = small([1500], [gen.random_tree(N, rng)], H, seed=41 + H, std_q=3.0)
+    check(x, chunk=256, what=f"{H * N} live rows")
+
+
 def test_batch_varlen_with_empty_prefix():
     rng = np.random.default_rng(3)
     parents = [np.array([-1], np.int32), gen.random_tree(5, rng), gen.chain_plus_branch(), gen.random_tree(17, rng)]
@@ -162,6 +171,16 @@ def test_config5_sampled_requests():
     x = gen.config_inputs(5)
     log(f"config 5 prefix lengths {[x.prefix_len(b) for b in range(8)]}")
     check(x, requests=[0, 3, 7], heads=[0, 9, 15], what="config 5 requests 0,3,7")
+
+
+def test_small_rows_decode_full():
+    x = gen.config_inputs(6)
+    check(x, what="decode 16 rows, 131072-token prefix")
+
+
+def test_small_rows_nine_queries_full():
+    x = gen.config_inputs(7)
+    check(x, what="9 nodes x 16 heads, 185000-token prefix")
 
 
 def test_determinism():
