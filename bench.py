@@ -51,7 +51,7 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
 # their sha256, and reported as null for any other build.
 MEASURED_TRAFFIC = {
     # sha256(prefix_splitkv.hip + kernels.h): (fetch KiB, write KiB, fetch scale, write scale)
-    "e6fd2291b30af722e933488c25568699266e653dd3dfd38280e69dbb3d1889b2": (59185.8, 31260.9, 2.0, 1.0),
+    "c019aaab41cbc53e04ca5691809669eb1398a369e6be911aecf2a9d330c2c980": (59493.3, 31260.9, 2.0, 1.0),
 }
 KERNEL_SOURCES = ("prefix_splitkv.hip", "kernels.h")
 KV_ROW_BYTES = 576 * 2
