@@ -212,6 +212,9 @@ def main():
     ap.add_argument("--launch", default="eager", choices=["eager", "graph"],
                     help="eager: one library call per step; graph: each step replays a captured HIP graph "
                          "of that call (one per pool copy)")
+    ap.add_argument("--device-lengths", action="store_true",
+                    help="pass VAMLA_FLAG_DEVICE_LENGTHS: lengths read from the device arrays and the chunk "
+                         "size chosen on the device (what a graph captured once for changing lengths runs)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 512 MiB device copy (counter calibration under rocprofv3 --pmc)")
@@ -235,6 +238,9 @@ def main():
     err(f"[bench] workload: {wname}  (inputs generated in {time.perf_counter() - t0:.1f} s)")
     alg = algorithmic(x)
     prob = vb.Problem.from_host(x.cu_prefix, x.cu_tree, x.num_heads, x.pool.shape[0], x.scale)
+    if args.device_lengths:
+        prob.flags = vb.FLAG_DEVICE_LENGTHS
+        wname += ", lengths read on the device"
     info = vb.plan(prob)
     err(f"[bench] plan: chunk={info.chunk} row_tiles={info.row_tiles} chunks={info.max_chunks} "
         f"grid={info.grid_items} workspace={info.workspace_bytes / 1e6:.1f} MB")

@@ -91,17 +91,39 @@ typedef struct vamla_params {
   int64_t pool_slots;       /* P >= 1: rows in kv_pool */
   float softmax_scale;      /* sigma > 0 (finite), applied to q.k before the exponential */
   int32_t max_tree;         /* >= every N_b, in [1, 65] (planning bound) */
-  int32_t total_tree;       /* T = cu_tree[B] >= 1; with B = 1 the kernels take the request's
-                               bounds from total_tree / total_prefix and do not read cu_* */
+  int32_t total_tree;       /* T = cu_tree[B] >= 1; with B = 1 (and no VAMLA_FLAG_DEVICE_LENGTHS)
+                               the kernels take the request's bounds from total_tree /
+                               total_prefix and do not read cu_* */
   int64_t max_prefix;       /* >= every L_b (planning bound), >= 0 */
   int64_t total_prefix;     /* cu_prefix[B]; chooses the chunk size (and is L when B = 1) */
   int32_t chunk;            /* prefix keys per split; multiple of 32, or 0 = choose automatically */
-  uint32_t flags;           /* reserved, must be 0 */
+  uint32_t flags;           /* 0 or VAMLA_FLAG_DEVICE_LENGTHS */
   const int32_t* cu_prefix; /* device [B+1], cu_prefix[0] = 0, non-decreasing */
   const int32_t* cu_tree;   /* device [B+1], cu_tree[0] = 0, increasing (N_b >= 1) */
   void* workspace;          /* device, 256-byte aligned, >= vamla_workspace_size bytes */
   size_t workspace_bytes;
 } vamla_params;
+
+/*
+ * VAMLA_FLAG_DEVICE_LENGTHS: the kernels read every length from the device
+ * arrays cu_prefix / cu_tree at run time (never from total_prefix /
+ * total_tree) and choose the chunk size on the device from the longest
+ * prefix they find there:
+ *     chunk = max(32, 32 * ceil(ceil(Lmax / max_chunks) / 32)),
+ * max_chunks being the plan's bound for max_prefix, so a request never has
+ * more chunks than the plan (and the workspace) allows and a shorter prefix
+ * still spreads over every chunk slot.  A captured HIP graph of a verify call
+ * with this flag stays valid while the caller rewrites cu_prefix / cu_tree
+ * (and the index arrays) between replays, as long as every L_b <= max_prefix,
+ * every N_b <= max_tree, cu_tree[B] <= total_tree and the buffers are sized
+ * for total_prefix / total_tree (the capture-time upper bounds).  Without the
+ * flag a call planned for one set of lengths must be re-captured when they
+ * change.  The split of a prefix into chunks can differ from the host plan's,
+ * so results can differ from a call without the flag by rounding only.
+ * ("The Anatomy of a Kernel Investigation", last section: the verify kernel
+ * of the live service runs under CUDA-graph capture.)
+ */
+#define VAMLA_FLAG_DEVICE_LENGTHS 1u
 
 /* Work decomposition the library derives from vamla_params (host only). */
 typedef struct vamla_plan_info {

@@ -23,6 +23,7 @@ MAX_TREE = 65
 MAX_HEADS = 128
 KEY_TILE = 32
 ROW_TILE = 64
+FLAG_DEVICE_LENGTHS = 1
 
 STATUS = {
     0: "VAMLA_OK", -1: "VAMLA_ERR_INVALID_ARG", -2: "VAMLA_ERR_UNSUPPORTED", -3: "VAMLA_ERR_WORKSPACE",
@@ -130,11 +131,12 @@ class Problem:
     max_prefix: int
     total_prefix: int
     chunk: int = 0
+    flags: int = 0
 
     def params(self, cu_prefix_ptr: int = 0, cu_tree_ptr: int = 0, workspace_ptr: int = 0,
                workspace_bytes: int = 0) -> VamlaParams:
         return VamlaParams(self.batch, self.num_heads, D_QK, D_V, self.pool_slots, self.softmax_scale,
-                           self.max_tree, self.total_tree, self.max_prefix, self.total_prefix, self.chunk, 0,
+                           self.max_tree, self.total_tree, self.max_prefix, self.total_prefix, self.chunk, self.flags,
                            cu_prefix_ptr, cu_tree_ptr, workspace_ptr, workspace_bytes)
 
     @staticmethod

@@ -37,6 +37,7 @@ struct PrefixArgs {
   int32_t total_prefix;       // = cu_prefix[B]; with B = 1 the kernel takes
   int32_t total_tree;         // the request's bounds from these two, not cu_*
   float scale_log2;           // softmax_scale * log2(e)
+  int32_t device_lengths;     // 1: lengths from cu_* only, chunk from device_chunk()
 };
 
 // LSE merge of the chunk partials.
@@ -56,7 +57,18 @@ struct MergeArgs {
   int32_t total_tree;
   int32_t row_bits;           // log2 of the rows a wave covers (<= 6): live rows of a tile, rounded up
   int32_t chunk_wave_bits;    // log2 of the waves that split one column group's chunks (<= 2)
+  int32_t device_lengths;     // as in PrefixArgs
 };
+
+// Chunk size chosen on the device from the longest prefix in cu_prefix: the
+// smallest multiple of the key tile that splits it into at most max_chunks
+// chunks (at least one tile).  Split and merge compute the same value.
+__device__ __forceinline__ int device_chunk(const int32_t* cu_prefix, int batch, int max_chunks) {
+  int lmax = 0;
+  for (int i = 0; i < batch; ++i) lmax = max(lmax, cu_prefix[i + 1] - cu_prefix[i]);
+  const int c = (lmax + max_chunks - 1) / max_chunks;
+  return max(kKeyTile, (c + kKeyTile - 1) / kKeyTile * kKeyTile);
+}
 
 hipError_t launch_prefix_splitkv(const PrefixArgs& a, hipStream_t stream);
 hipError_t launch_lse_merge(const MergeArgs& a, hipStream_t stream);

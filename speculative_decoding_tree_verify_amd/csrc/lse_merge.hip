@@ -69,14 +69,16 @@ __global__ __launch_bounds__(64 * kWaves) void lse_merge_kernel(MergeArgs a) {
   const int tile = item - b * a.row_tiles;
   const int cw_bits = a.chunk_wave_bits;
   const int CW = 1 << cw_bits;
-  // a single request's bounds are the call's totals (no load before the partials')
-  const bool one = a.batch == 1;
+  // a single request's bounds are the call's totals (no load before the
+  // partials'), unless the lengths are to be read on the device
+  const bool one = a.batch == 1 && !a.device_lengths;
+  const int chunk = a.device_lengths ? device_chunk(a.cu_prefix, a.batch, a.max_chunks) : a.chunk;
   const int t0 = one ? 0 : a.cu_tree[b];
   const int rows_b = ((one ? a.total_tree : a.cu_tree[b + 1]) - t0) * a.num_heads;
   if (tile * kRowTile >= rows_b) return;
   const int L = one ? a.total_prefix : a.cu_prefix[b + 1] - a.cu_prefix[b];
   // a prefix longer than max_prefix is a caller error; never read past the plan
-  const int S = max(1, min((L + a.chunk - 1) / a.chunk, a.max_chunks));
+  const int S = max(1, min((L + chunk - 1) / chunk, a.max_chunks));
 
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;

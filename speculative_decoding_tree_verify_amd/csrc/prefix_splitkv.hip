@@ -238,10 +238,13 @@ __global__ __launch_bounds__(512, 1) void prefix_splitkv_kernel(PrefixArgs a) {
   // node have no items.  Past kCompactBatch requests the per-workgroup scan
   // would cost more than it saves, and the padded grid is used as it is.
   int b, s, tile;
-  const int chunk = a.chunk, max_chunks = a.max_chunks;
-  // A single request's bounds are the call's totals: nothing is loaded
-  // before the first tile's slot indices.
-  const bool one = a.batch == 1;
+  const int max_chunks = a.max_chunks;
+  const int chunk = a.device_lengths ? __builtin_amdgcn_readfirstlane(device_chunk(a.cu_prefix, a.batch, max_chunks))
+                                     : a.chunk;
+  // A single request's bounds are the call's totals (unless the lengths are
+  // to be read on the device): nothing is loaded before the first tile's
+  // slot indices.
+  const bool one = a.batch == 1 && !a.device_lengths;
   const int one_L = a.total_prefix, one_N = a.total_tree;
   auto len_p = [&](int i) -> int { return one ? one_L : a.cu_prefix[i + 1] - a.cu_prefix[i]; };
   auto len_t = [&](int i) -> int { return one ? one_N : a.cu_tree[i + 1] - a.cu_tree[i]; };

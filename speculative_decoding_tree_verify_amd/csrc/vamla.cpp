@@ -42,7 +42,7 @@ int check_shape(const vamla_params* p) {
   if (!p) return VAMLA_ERR_INVALID_ARG;
   if (p->batch < 1 || p->pool_slots < 1 || p->max_prefix < 0 || p->total_prefix < 0 || p->total_tree < 1)
     return VAMLA_ERR_INVALID_ARG;
-  if (p->flags != 0) return VAMLA_ERR_INVALID_ARG;
+  if ((p->flags & ~VAMLA_FLAG_DEVICE_LENGTHS) != 0) return VAMLA_ERR_INVALID_ARG;
   if (!(std::isfinite(p->softmax_scale) && p->softmax_scale > 0.f)) return VAMLA_ERR_INVALID_ARG;
   if (p->d_qk != VAMLA_D_QK || p->d_v != VAMLA_D_V) return VAMLA_ERR_UNSUPPORTED;
   if (p->num_heads < 1 || p->num_heads > VAMLA_MAX_HEADS) return VAMLA_ERR_UNSUPPORTED;
@@ -164,6 +164,7 @@ int split_launch(const vamla_params* p, const vamla_plan_info& pl, const uint16_
   a.total_prefix = (int32_t)p->total_prefix;
   a.total_tree = p->total_tree;
   a.scale_log2 = p->softmax_scale * 1.4426950408889634f;
+  a.device_lengths = (p->flags & VAMLA_FLAG_DEVICE_LENGTHS) ? 1 : 0;
   return launch_prefix_splitkv(a, stream) == hipSuccess ? VAMLA_OK : VAMLA_ERR_LAUNCH;
 }
 
@@ -182,6 +183,7 @@ int merge_launch(const vamla_params* p, const vamla_plan_info& pl, uint16_t* out
   a.batch = p->batch;
   a.total_prefix = (int32_t)p->total_prefix;
   a.total_tree = p->total_tree;
+  a.device_lengths = (p->flags & VAMLA_FLAG_DEVICE_LENGTHS) ? 1 : 0;
   // a wave covers the live rows of a tile (at most max_tree * H when there is
   // one row tile), its other lanes split the chunks
   const int64_t tile_rows = std::min<int64_t>(kRowTile, (int64_t)p->max_tree * p->num_heads);

@@ -223,3 +223,18 @@ def test_validate_catches_bad_slots_and_lengths(L):
     assert vb.validate(p, x.parent, x.cu_tree, cp) == -8
     p2 = vb.Problem(**{**p.__dict__, "max_tree": 8})
     assert vb.validate(p2, x.parent, x.cu_tree, x.cu_prefix) == -8
+
+
+def test_flags(L):
+    # only VAMLA_FLAG_DEVICE_LENGTHS is defined; it does not change the plan
+    p = prob(3)
+    base = vb.plan(p)
+    p.flags = vb.FLAG_DEVICE_LENGTHS
+    info = vb.plan(p)
+    assert (info.chunk, info.max_chunks, info.grid_items, info.workspace_bytes) == \
+        (base.chunk, base.max_chunks, base.grid_items, base.workspace_bytes)
+    for bad in (2, 4, 1 << 31, 3):
+        p.flags = bad
+        with pytest.raises(vb.VamlaError) as e:
+            vb.plan(p)
+        assert e.value.status == -1

@@ -78,3 +78,62 @@ def test_captured_step_replays_bit_identical(config):
         assert torch.equal(lse_g, ref_lse), f"replay {r}: lse differs"
         log(f"[case] replay {r} bit-identical")
     d["q"].copy_(q0)
+
+
+@pytest.mark.parametrize("cap,variants", [
+    ([3000, 3000], [(3000, 3000), (1500, 2999), (0, 1), (700, 2), (3000, 0)]),
+    ([5000], [(5000,), (1,), (0,), (2500,), (4097,)]),
+])
+def test_one_capture_serves_changing_prefix_lengths(cap, variants):
+    # VAMLA_FLAG_DEVICE_LENGTHS: lengths are read from cu_prefix / cu_tree on
+    # the device and the chunk size is chosen there, so one graph captured for
+    # the upper bounds replays correctly after the caller rewrites the lengths
+    # and the slot list (a single request included, whose bounds otherwise come
+    # from the host totals baked into the launch)
+    import torch
+    log(f"[case] device lengths, capacity {cap}, variants {variants}")
+    rng = np.random.default_rng(len(cap))
+    parents = [gen.random_tree(9, rng), gen.bounded_tree(5, rng)][:len(cap)]
+    x = gen.make_inputs(cap, parents, 8, sum(cap) + 64 + 300, "scrambled", seed=90 + len(cap))
+    d = to_dev(x)
+    p = problem(x)
+    p.flags = vb.FLAG_DEVICE_LENGTHS
+    ws_g, ws_e = vb.Workspace(p), vb.Workspace(p)
+    T, H = x.total_tree, x.num_heads
+    out_g = torch.empty((T, H, 512), dtype=torch.bfloat16, device="cuda")
+    lse_g = torch.empty((T, H), dtype=torch.float32, device="cuda")
+    full = [x.prefix_slot_idx[x.cu_prefix[b]:x.cu_prefix[b + 1]] for b in range(x.batch)]
+
+    def step():
+        vb.verify_attn_mla(p, d["q"], d["kv_pool"], d["prefix_slot_idx"], d["tree_slot_idx"], d["parent"],
+                           d["cu_prefix"], d["cu_tree"], ws=ws_g, out=out_g, lse=lse_g)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+
+    for lens in variants:
+        idx = np.concatenate([full[b][:lens[b]] for b in range(x.batch)]).astype(np.int32)
+        cu_p = np.zeros(x.batch + 1, np.int32)
+        cu_p[1:] = np.cumsum(lens)
+        d["prefix_slot_idx"][:len(idx)].copy_(torch.from_numpy(idx))
+        d["cu_prefix"].copy_(torch.from_numpy(cu_p))
+        out_g.fill_(float("nan"))
+        lse_g.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        ref_out, ref_lse = _eager(p, d, ws_e)
+        assert torch.equal(out_g.view(torch.int16), ref_out.view(torch.int16)), f"lengths {lens}: replay differs"
+        assert torch.equal(lse_g, ref_lse), f"lengths {lens}: replay lse differs"
+        ro, rl = vo.verify(x.q, x.pool, idx, x.tree_slot_idx, x.parent, cu_p, x.cu_tree, x.scale)
+        assert_close_lse(lse_g.cpu().numpy().astype(np.float64), rl, f"lengths {lens}")
+        assert_close_out(out_g.float().cpu().numpy().astype(np.float64), ro, f"lengths {lens}")
+        log(f"[case] lengths {lens}: replay matches eager bit for bit and the oracle")
