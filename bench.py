@@ -215,6 +215,9 @@ def main():
     ap.add_argument("--device-lengths", action="store_true",
                     help="pass VAMLA_FLAG_DEVICE_LENGTHS: lengths read from the device arrays and the chunk "
                          "size chosen on the device (what a graph captured once for changing lengths runs)")
+    ap.add_argument("--defrag", action="store_true",
+                    help="each step first gathers the call's prefix and tree rows into a contiguous pool "
+                         "(vamla_slot_gather) and verifies on that copy")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 512 MiB device copy (counter calibration under rocprofv3 --pmc)")
@@ -264,6 +267,31 @@ def main():
     def eager_step(i):
         vb.verify_attn_mla(prob, q, pools[i % n_copies], pre, tre, par, cup, cut, ws=ws, out=out, lse=lse)
 
+    defrag = None
+    if args.defrag:
+        # compacted copy: prefix rows of every request, then the tree rows, in
+        # logical order, so the slot lists become ranges
+        n_rows = x.total_prefix + x.total_tree
+        idx_all = torch.cat([pre[:x.total_prefix], tre])
+        dst = torch.empty((n_rows, 576), dtype=torch.bfloat16, device=dev)
+        pre_c = torch.arange(0, max(x.total_prefix, 1), dtype=torch.int32, device=dev)
+        tre_c = torch.arange(x.total_prefix, n_rows, dtype=torch.int32, device=dev)
+        prob_c = vb.Problem.from_host(x.cu_prefix, x.cu_tree, x.num_heads, n_rows, x.scale)
+        prob_c.flags = prob.flags
+        ws_c = vb.Workspace(prob_c)
+
+        def gather_only(i):
+            vb.slot_gather(pools[i % n_copies], idx_all, dst)
+
+        def verify_contiguous(i):
+            vb.verify_attn_mla(prob_c, q, dst, pre_c, tre_c, par, cup, cut, ws=ws_c, out=out, lse=lse)
+
+        def eager_step(i):  # noqa: F811
+            gather_only(i)
+            verify_contiguous(i)
+        defrag = dict(gather=gather_only, verify=verify_contiguous, rows=n_rows)
+        wname += ", defragmented each step (slot gather + verify on the contiguous copy)"
+
     step = eager_step
     if args.launch == "graph":
         side = torch.cuda.Stream()
@@ -307,6 +335,15 @@ def main():
 
     # --- per-kernel durations (HIP events on the launch stream) ---
     iters = max(20, min(args.steps, 200))
+    defrag_us = None
+    if defrag is not None:
+        ms_g = time_events(defrag["gather"], iters)
+        ms_v = time_after(defrag["gather"], defrag["verify"], iters)
+        defrag_us = {"slot_gather": round(ms_g * 1e3, 2), "verify_on_contiguous": round(ms_v * 1e3, 2),
+                     "rows": defrag["rows"]}
+        err(f"[bench] defrag: slot gather of {defrag['rows']} rows {ms_g * 1e3:.1f} us "
+            f"({2 * defrag['rows'] * KV_ROW_BYTES / (ms_g * 1e-3) / 1e9:.0f} GB/s read + written), "
+            f"verify on the contiguous copy {ms_v * 1e3:.1f} us")
     ms_split = time_events(split_only, iters)
     ms_merge = time_after(split_only, merge_only, iters)
     ms_step_ev = time_events(step, iters)
@@ -370,6 +407,7 @@ def main():
             "step_us_warm_p10_p50_p90": warm,
             "device_copy_gbs": round(copy_gbs, 1) if copy_gbs else None,
             "pct_of_device_copy": round(value / copy_gbs * 100, 3) if copy_gbs else None,
+            "defrag_us": defrag_us,
         },
         "roofline": roofline_of_split(t_mfma >= t_hbm, flops, alg, ms_split,
                                       split_kernel_traffic() if args.config == 3 and not args.slot_mode else None),
