@@ -35,11 +35,12 @@ def problem(x: gen.VerifyInputs, chunk: int = 0) -> vb.Problem:
     return vb.Problem.from_host(x.cu_prefix, x.cu_tree, x.num_heads, x.pool.shape[0], x.scale, chunk=chunk)
 
 
-def run_verify(x: gen.VerifyInputs, chunk: int = 0, dev=None):
+def run_verify(x: gen.VerifyInputs, chunk: int = 0, dev=None, flags: int = 0):
     """Returns (out fp64 [T,H,512], lse fp64 [T,H]) from the HIP path."""
     import torch
     d = dev or to_dev(x)
     p = problem(x, chunk)
+    p.flags = flags
     out, lse = vb.verify_attn_mla(p, d["q"], d["kv_pool"], d["prefix_slot_idx"], d["tree_slot_idx"], d["parent"],
                                   d["cu_prefix"], d["cu_tree"])
     torch.cuda.synchronize()

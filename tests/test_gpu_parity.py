@@ -23,9 +23,10 @@ def oracle_full(x, heads=None, requests=None):
                      x.scale, heads=heads, requests=requests)
 
 
-def check(x, chunk=0, heads=None, requests=None, what=""):
-    log(f"[case] {what} B={x.batch} H={x.num_heads} T={x.total_tree} prefix={x.total_prefix} chunk={chunk}")
-    out, lse, _ = run_verify(x, chunk)
+def check(x, chunk=0, heads=None, requests=None, what="", flags=0):
+    log(f"[case] {what} B={x.batch} H={x.num_heads} T={x.total_tree} prefix={x.total_prefix} chunk={chunk} "
+        f"flags={flags}")
+    out, lse, _ = run_verify(x, chunk, flags=flags)
     ro, rl = oracle_full(x, heads, requests)
     sel = np.isfinite(rl)
     assert sel.any()
@@ -70,15 +71,16 @@ def test_batch_varlen_with_empty_prefix():
     check(x, chunk=192, what="batch varlen")
 
 
+@pytest.mark.parametrize("flags", [0, vb.FLAG_DEVICE_LENGTHS])
 @pytest.mark.parametrize("batch", [40, 70])
-def test_many_requests(batch):
+def test_many_requests(batch, flags):
     # up to 64 requests the split kernel lists the real work items and spreads
     # them over the XCDs; past that it walks the padded item grid
     rng = np.random.default_rng(30 + batch)
     lens = [int(v) for v in rng.integers(0, 400, batch)]
     parents = [gen.random_tree(int(n), rng) for n in rng.integers(1, 10, batch)]
     x = small(lens, parents, 2, seed=31 + batch)
-    check(x, chunk=128, what=f"{batch} requests")
+    check(x, chunk=128, what=f"{batch} requests", flags=flags)
 
 
 def test_single_request_bounds_match_the_batched_path():
