@@ -596,11 +596,6 @@ __global__ __launch_bounds__(512, 1) void prefix_splitkv_kernel(PrefixArgs a) {
         bf16x8 pop[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) pop[i] = ds_b128(pb_addr[it & 1], i * 1024);
-        // the gather of tile it+2 is issued while P(it-2) is in flight
-        if (do_dma) {
-#pragma unroll
-          for (int d = 0; d < 9; ++d) gather_one(a.pool, svd, dbuf, c, lane, d);
-        }
 #pragma unroll
         for (int f = 0; f < 8; ++f) {
           const int ks = f >> 2, cb = f & 3;
@@ -611,6 +606,15 @@ __global__ __launch_bounds__(512, 1) void prefix_splitkv_kernel(PrefixArgs a) {
             if (rb == 0 || rb1_live)
               o[cb + 4 * rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[f], pop[j], o[cb + 4 * rb], 0, 0, 0);
             if (rb == 1) vf[f] = vread(nslot, f);  // V(it-1); at it = ntiles+1 a harmless re-read
+            __builtin_amdgcn_sched_barrier(0);
+          }
+          // the gather of tile it+2, issued once the first four MFMAs are
+          // under way: issued before them, its address arithmetic kept the
+          // matrix core idle at the top of the iteration; issued later, the
+          // rows arrive late
+          if (f == 1 && do_dma) {
+#pragma unroll
+            for (int d = 0; d < 9; ++d) gather_one(a.pool, svd, dbuf, c, lane, d);
             __builtin_amdgcn_sched_barrier(0);
           }
         }
