@@ -238,3 +238,14 @@ def test_flags(L):
         with pytest.raises(vb.VamlaError) as e:
             vb.plan(p)
         assert e.value.status == -1
+
+
+def test_bench_refuses_more_than_one_gpu():
+    # the path runs on one GPU; bench.py says so instead of measuring
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr or "single MI355X" in r.stderr
