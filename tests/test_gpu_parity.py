@@ -131,20 +131,23 @@ def test_sharp_scores_move_the_reference():
     check(x, chunk=1024, what="sharp scores")
 
 
+@pytest.mark.parametrize("H,N,node,head", [(2, 5, 2, 1), (5, 9, 8, 4)])
 @pytest.mark.parametrize("chunk", [2048, 32])
-def test_reference_jump_mid_chunk(chunk):
+def test_reference_jump_mid_chunk(chunk, H, N, node, head):
     # one prefix key deep inside a chunk gets a score far above everything
-    # before it, so the running reference max has to move mid-chunk; with
-    # 32-key chunks the key sits in chunk 46 of 63, past the merge's first
-    # batch of 32 partials, so the merge's running max moves too
+    # before it, so the chunk's softmax reference has to move mid-chunk; with
+    # 32-key chunks the key sits in chunk 46 of 63, and the merge's fold over
+    # chunk lanes and waves has to move its max too.  10 and 45 live rows:
+    # the row with the jump sits in a tile with dead 16-row halves (row 44
+    # is in the second row pair, whose upper half is dead)
     rng = np.random.default_rng(7)
-    x = small([2000], [gen.random_tree(5, rng)], 2, seed=19)
+    x = small([2000], [gen.random_tree(N, rng)], H, seed=19)
     key = 1500
     slot = x.prefix_slot_idx[key]
     k = vo.bf16_bits_to_f64(x.pool[slot])
-    x.q[2, 1] = gen.f32_to_bf16_bits((k * 40.0).astype(np.float32))                  # score ~ 40*|k|^2*sigma
-    out, lse = check(x, chunk=chunk, what=f"reference jump chunk={chunk}")
-    np.testing.assert_allclose(out[2, 1], k[:512], atol=2e-2)
+    x.q[node, head] = gen.f32_to_bf16_bits((k * 40.0).astype(np.float32))            # score ~ 40*|k|^2*sigma
+    out, lse = check(x, chunk=chunk, what=f"reference jump chunk={chunk} rows={H * N} node={node} head={head}")
+    np.testing.assert_allclose(out[node, head], k[:512], atol=2e-2)
 
 
 def test_config1():
