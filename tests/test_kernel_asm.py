@@ -1,0 +1,95 @@
+"""Checks on the gfx950 assembly of the split kernel (CPU only: hipcc
+cross-compiles, nothing runs).
+
+The PV waves issue their LDS reads as inline asm and wait for them with
+hand-counted lgkmcnt values, so the compiler does not know when those
+registers are written.  If it ever copies such a register (a phi move at a
+branch join, a spill) between the read and its wait, the copy holds stale
+data and the results are silently wrong.  This test compiles the kernel
+exactly as the library build does and scans the PV key loop for any move
+that reads the destination of an LDS read not yet covered by an
+lgkmcnt(0); it also checks that no VGPR spills to scratch memory.
+"""
+
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+
+from speculative_decoding_tree_verify_amd import build as vbuild
+
+CSRC = vbuild.CSRC
+
+
+def _hipcc():
+    try:
+        return vbuild.hipcc()
+    except RuntimeError:
+        return None
+
+
+@pytest.fixture(scope="module")
+def asm(tmp_path_factory):
+    cc = _hipcc()
+    if cc is None or shutil.which(cc) is None and not os.path.exists(cc):
+        pytest.skip("hipcc not available")
+    out = tmp_path_factory.mktemp("asm") / "split.s"
+    flags = [f for f in vbuild.HIP_FLAGS if f not in ("-fPIC",)]
+    cmd = [cc, *flags, "--cuda-device-only", "-S", "-I", vbuild.INCLUDE, "-I", CSRC, "-o", str(out),
+           os.path.join(CSRC, "prefix_splitkv.hip")]
+    r = subprocess.run(cmd, capture_output=True, text=True, timeout=600)
+    assert r.returncode == 0, r.stderr[-2000:]
+    return out.read_text()
+
+
+def _regs(tok):
+    m = re.match(r"v\[(\d+):(\d+)\]", tok)
+    if m:
+        return set(range(int(m.group(1)), int(m.group(2)) + 1))
+    m = re.match(r"v(\d+)$", tok)
+    return {int(m.group(1))} if m else set()
+
+
+def _pv_loop(lines):
+    """Line range of the PV waves' key loop: the innermost loop holding the
+    32x32x16 MFMAs, from its header label to its back-edge branch."""
+    idx = [i for i, l in enumerate(lines) if "v_mfma_f32_32x32x16" in l]
+    assert idx, "no 32x32x16 MFMA in the kernel"
+    a = max(i for i in range(idx[0]) if lines[i].startswith(".LBB") and "Parent Loop" in lines[i])
+    b = min(i for i in range(idx[-1], len(lines)) if "s_cbranch_execz" in lines[i])
+    return a, b
+
+
+def test_no_copies_of_lds_reads_in_flight(asm):
+    lines = asm.splitlines()
+    a, b = _pv_loop(lines)
+    inflight, bad, n_reads = set(), [], 0
+    for i in range(a, b + 1):
+        s = lines[i].strip()
+        if not s or s.startswith((";", ".")):
+            continue
+        op = s.split()[0]
+        if op.startswith("ds_read"):
+            inflight |= _regs(s.split()[1].rstrip(","))
+            n_reads += 1
+            continue
+        if op == "s_waitcnt" and "lgkmcnt(0)" in s:
+            inflight = set()
+            continue
+        if op.startswith(("v_mov", "v_cndmask", "v_accvgpr", "v_perm", "v_writelane")):
+            srcs = set()
+            for t in s.split()[2:]:
+                srcs |= _regs(t.rstrip(","))
+            if srcs & inflight:
+                bad.append(f"line {i + 1}: {s}")
+    assert n_reads >= 16, "PV loop not found where expected"
+    assert not bad, "registers of LDS reads still in flight are copied:\n" + "\n".join(bad[:10])
+
+
+def test_no_vgpr_spills(asm):
+    spills = [int(v) for v in re.findall(r"\.vgpr_spill_count:\s+(\d+)", asm)]
+    scratch = [int(v) for v in re.findall(r"\.private_segment_fixed_size:\s+(\d+)", asm)]
+    assert spills and max(spills) == 0
+    assert scratch and max(scratch) == 0
