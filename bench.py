@@ -195,7 +195,14 @@ def cpu_baseline(x: gen.VerifyInputs, kv_bytes: int, budget_s: float = 20.0):
         if time.perf_counter() + times[-1] > t_end or len(times) >= 5:
             break
     t = float(np.median(times))
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), None)
+    except OSError:
+        pass
     return {"value": round(kv_bytes / t / 1e9, 4), "unit": "GB/s", "cores": int(cores), "kind": "oracle",
+            "cpu_model": model,
             "sample": f"full verify step of the same workload (all heads and nodes), fp64 numpy, "
                       f"{len(times)} run(s), median {t * 1e3:.1f} ms/step",
             "ms_per_step": round(t * 1e3, 3)}
