@@ -62,10 +62,16 @@ struct MergeArgs {
 
 // Chunk size chosen on the device from the longest prefix in cu_prefix: the
 // smallest multiple of the key tile that splits it into at most max_chunks
-// chunks (at least one tile).  Split and merge compute the same value.
+// chunks (at least one tile).  Split and merge compute the same value.  Each
+// lane reads every 64th request's length (one round of loads in flight
+// however large the batch), then the wave takes the max across lanes; every
+// lane of the wave must be active.
 __device__ __forceinline__ int device_chunk(const int32_t* cu_prefix, int batch, int max_chunks) {
+  const int lane = threadIdx.x & 63;
   int lmax = 0;
-  for (int i = 0; i < batch; ++i) lmax = max(lmax, cu_prefix[i + 1] - cu_prefix[i]);
+  for (int i = lane; i < batch; i += 64) lmax = max(lmax, cu_prefix[i + 1] - cu_prefix[i]);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) lmax = max(lmax, __shfl_xor(lmax, off));
   const int c = (lmax + max_chunks - 1) / max_chunks;
   return max(kKeyTile, (c + kKeyTile - 1) / kKeyTile * kKeyTile);
 }

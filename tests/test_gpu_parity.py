@@ -72,7 +72,7 @@ def test_batch_varlen_with_empty_prefix():
 
 
 @pytest.mark.parametrize("flags", [0, vb.FLAG_DEVICE_LENGTHS])
-@pytest.mark.parametrize("batch", [40, 70])
+@pytest.mark.parametrize("batch", [40, 70, 300])
 def test_many_requests(batch, flags):
     # up to 64 requests the split kernel lists the real work items and spreads
     # them over the XCDs; past that it walks the padded item grid
