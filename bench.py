@@ -51,7 +51,7 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
 # their sha256, and reported as null for any other build.
 MEASURED_TRAFFIC = {
     # sha256(prefix_splitkv.hip + kernels.h): (fetch KiB, write KiB, fetch scale, write scale)
-    "efe2b1ac549d1d9f1d02789ef1161c1159e818c44044476ca955ee9995e9d66f": (59208.1, 31260.9, 2.0, 1.0),
+    "190e069271bcba886b49308bcb5ce3358ca784d9155afbbf36a886ff0507236f": (59208.1, 31260.9, 2.0, 1.0),
 }
 KERNEL_SOURCES = ("prefix_splitkv.hip", "kernels.h")
 KV_ROW_BYTES = 576 * 2

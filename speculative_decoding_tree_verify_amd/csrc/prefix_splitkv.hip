@@ -30,8 +30,13 @@
 // t and turn the scores of tile t-1 into P(t-1) (that softmax runs while tile
 // t's first K fragments are in flight); the PV waves multiply V(t-2), read
 // into VGPRs during iteration t-1, by P(t-2), read V(t-1) fragment by
-// fragment as the registers free up, and gather tile t+2.  The restart vote
-// of tile t-2 is read early and tested just before the barrier.
+// fragment as the registers free up, and gather tile t+2 once their first
+// four MFMAs are under way.  The restart vote of tile t-2 is read early and
+// tested just before the barrier.  A tile whose query rows end inside it
+// skips the MFMAs of its dead 16-row halves (QK; with no live row in a pair,
+// its K reads too) and of rows 32..63 (PV) when they hold no live row.
+// With the request lengths read on the device, the chunk size comes from
+// the longest prefix in cu_prefix (device_chunk) instead of the host plan.
 //
 // Gather: LDS-DMA moves 16 bytes per lane straight into LDS.  Latent rows: one
 // 64-lane buffer_load_dwordx4 ... lds per key with a per-row descriptor; rope
