@@ -190,10 +190,17 @@ int merge_launch(const vamla_params* p, const vamla_plan_info& pl, uint16_t* out
   int bits = 0;
   while ((1 << bits) < tile_rows) ++bits;
   a.row_bits = bits;
-  // waves per column group that split its chunks: as few as keep >= 512
-  // workgroups (2 per CU) in the grid
+  // waves per column group that split its chunks: one when the grid has
+  // >= 512 workgroups (2 per CU) or when one thread's chunks fit in one batch
+  // of loads (16); otherwise the fewest that bring a thread's share of the
+  // chunks to one batch (at most 4).  Splitting costs an exchange through
+  // LDS, so it pays only where it removes a round trip.
   const int64_t base = (int64_t)p->batch * pl.row_tiles * (kD4 / 4);
-  a.chunk_wave_bits = base >= 512 ? 0 : base >= 256 ? 1 : 2;
+  const int64_t lanes_per_row = 64 >> bits;   // chunk lanes of a wave
+  auto batches = [&](int cw) { return ceil_div(ceil_div(pl.max_chunks, lanes_per_row << cw), 16); };
+  int cw_bits = 0;
+  if (base < 512 && batches(0) > 1) cw_bits = batches(1) == 1 ? 1 : 2;
+  a.chunk_wave_bits = cw_bits;
   return launch_lse_merge(a, stream) == hipSuccess ? VAMLA_OK : VAMLA_ERR_LAUNCH;
 }
 
