@@ -43,7 +43,8 @@
  *     except VAMLA_ERR_LAUNCH, which reports a failed kernel launch.
  *   - Contents of index arrays (slot indices in [0, pool_slots), parent arrays,
  *     cumulative lengths) are the caller's contract: the GPU path does not check
- *     them.  vamla_validate checks them on host copies.
+ *     them unless VAMLA_FLAG_DEBUG_VALIDATE is set.  vamla_validate checks them
+ *     on host copies.
  *   - Entry points are reentrant; concurrent calls must use distinct workspaces.
  */
 #ifndef VAMLA_H
@@ -97,7 +98,7 @@ typedef struct vamla_params {
   int64_t max_prefix;       /* >= every L_b (planning bound), >= 0 */
   int64_t total_prefix;     /* cu_prefix[B]; chooses the chunk size (and is L when B = 1) */
   int32_t chunk;            /* prefix keys per split; multiple of 32, or 0 = choose automatically */
-  uint32_t flags;           /* 0 or VAMLA_FLAG_DEVICE_LENGTHS */
+  uint32_t flags;           /* 0 or an OR of VAMLA_FLAG_DEVICE_LENGTHS, VAMLA_FLAG_DEBUG_VALIDATE */
   const int32_t* cu_prefix; /* device [B+1], cu_prefix[0] = 0, non-decreasing */
   const int32_t* cu_tree;   /* device [B+1], cu_tree[0] = 0, increasing (N_b >= 1) */
   void* workspace;          /* device, 256-byte aligned, >= vamla_workspace_size bytes */
@@ -125,6 +126,31 @@ typedef struct vamla_params {
  */
 #define VAMLA_FLAG_DEVICE_LENGTHS 1u
 
+/*
+ * VAMLA_FLAG_DEBUG_VALIDATE: before the verify kernels, one more kernel on the
+ * same stream checks on the device what vamla_validate checks on the host
+ * (cumulative lengths against the params, the parent arrays, every slot index
+ * against pool_slots), for callers whose index data never leaves the GPU
+ * (graph capture with static buffers: "Mapping the Optimization Landscape for
+ * DDTree Verify Attention", "Input Knowledge Required to Understand This
+ * Message", item 5).  It writes the first violation, in the order
+ * (cu arrays by request, parent by node, prefix_slot_idx by position,
+ * tree_slot_idx by node), to the debug record in the workspace
+ * (vamla_plan_info.off_debug_record): int32[4] = {status, array, index,
+ * restarts}, status being VAMLA_ERR_INVALID_LENGTHS / _TREE / _SLOT and
+ * array 0 (cu_*), 1 (parent), 2 (prefix_slot_idx) or 3 (tree_slot_idx); the
+ * first three are zero when the data is valid.  restarts counts the chunk
+ * restarts of the split pass (a score more than 2^40 above a chunk's softmax
+ * reference makes a work item start over with a higher one; see the split
+ * kernel).  When the record is set, the split kernel does no work (no
+ * index is dereferenced) and the merge writes NaN to every element of out and
+ * lse (total_tree x H rows).  The call itself still returns VAMLA_OK: the
+ * check runs asynchronously and the caller reads the record when it syncs.
+ * With vamla_lse_merge alone, the merge reads the record the preceding
+ * vamla_split_partials call on the same workspace wrote.
+ */
+#define VAMLA_FLAG_DEBUG_VALIDATE 2u
+
 /* Work decomposition the library derives from vamla_params (host only). */
 typedef struct vamla_plan_info {
   int32_t chunk;            /* prefix keys per split (multiple of 32) */
@@ -134,25 +160,47 @@ typedef struct vamla_plan_info {
   /* workspace layout (byte offsets from vamla_params.workspace) */
   size_t off_part_o;        /* float [B][row_tiles][max_chunks][128 d4][64 rows][4] */
   size_t off_part_lse;      /* float [B][row_tiles][max_chunks][64 rows] */
+  size_t off_debug_record;  /* int32 [4], written only with VAMLA_FLAG_DEBUG_VALIDATE */
   size_t workspace_bytes;   /* total */
 } vamla_plan_info;
 
-/* Human-readable name of a status code (static string). */
+/*
+ * Human-readable name of a status code (static string, never NULL; unknown
+ * codes give "unknown status").  Host only.  Part of the error contract that
+ * lets a capture-safe call report failures without throwing or aborting
+ * ("Mapping the Optimization Landscape ...", "Input Knowledge Required to
+ * Understand This Message", item 5).
+ */
 const char* vamla_status_string(int status);
 
 /*
  * Derives the work decomposition and workspace layout.  Host only; makes no
  * HIP call, so it works without a GPU.  Returns VAMLA_ERR_INVALID_ARG or
- * VAMLA_ERR_UNSUPPORTED for parameters the kernels cannot take.  Pointer fields
- * of *p are not read.
+ * VAMLA_ERR_UNSUPPORTED for parameters the kernels cannot take (among them
+ * total_prefix > batch * max_prefix and total_tree > batch * max_tree).
+ * Pointer fields of *p are not read; *out is written only on VAMLA_OK.  The
+ * chunk split is the split-KV design of "The Anatomy of a Kernel
+ * Investigation", "The Reasoning Process: A Deep Dive", Phase 2 (a dense
+ * prefix in pieces, merged by log-sum-exp); the caller-owned workspace it
+ * sizes is the static buffer a graph-captured call needs ("Mapping the
+ * Optimization Landscape ...", "Input Knowledge ...", item 5).
  */
 int vamla_plan(const vamla_params* p, vamla_plan_info* out);
 
-/* Workspace bytes verify_attn_mla needs for *p (host only, like vamla_plan). */
+/*
+ * Workspace bytes verify_attn_mla needs for *p (host only, like vamla_plan;
+ * *bytes is written only on VAMLA_OK).  The caller allocates it once and
+ * reuses it across calls and graph replays ("Mapping the Optimization
+ * Landscape ...", "Input Knowledge ...", item 5: static buffers).
+ */
 int vamla_workspace_size(const vamla_params* p, size_t* bytes);
 
 /*
- * Host-side check of the index data a caller is about to pass (host copies):
+ * Host-side check of the index data a caller is about to pass (host copies;
+ * the slot and parent conventions are those of "The Anatomy of a Kernel
+ * Investigation", "The Bash Command": page_size=1 slots, and "Mapping the
+ * Optimization Landscape ...", "Input Knowledge ...", item 1: each draft
+ * token sees its ancestors).  Reads the host arrays only during the call:
  *   h_cu_prefix[B+1], h_cu_tree[B+1]: start at 0, prefix non-decreasing, tree
  *     increasing; totals match total_prefix / total_tree; every N_b <= max_tree,
  *     every L_b <= max_prefix;

@@ -24,6 +24,7 @@ MAX_HEADS = 128
 KEY_TILE = 32
 ROW_TILE = 64
 FLAG_DEVICE_LENGTHS = 1
+FLAG_DEBUG_VALIDATE = 2
 
 STATUS = {
     0: "VAMLA_OK", -1: "VAMLA_ERR_INVALID_ARG", -2: "VAMLA_ERR_UNSUPPORTED", -3: "VAMLA_ERR_WORKSPACE",
@@ -64,6 +65,7 @@ class VamlaPlanInfo(ctypes.Structure):
         ("grid_items", ctypes.c_int32),
         ("off_part_o", ctypes.c_size_t),
         ("off_part_lse", ctypes.c_size_t),
+        ("off_debug_record", ctypes.c_size_t),
         ("workspace_bytes", ctypes.c_size_t),
     ]
 
@@ -221,6 +223,8 @@ class Workspace:
 
     def __init__(self, prob: Problem, device=None):
         torch = _torch()
+        if device is not None and torch.device(device).type != "cuda":
+            raise ValueError("the workspace must be on the GPU")
         self.nbytes = workspace_size(prob)
         # 256-byte alignment: torch's caching allocator returns 512-byte aligned blocks
         self.buf = torch.empty(max(self.nbytes, 256), dtype=torch.uint8, device=device or "cuda")
@@ -232,23 +236,77 @@ class Workspace:
 
 
 def _params(prob: Problem, cu_prefix, cu_tree, ws: Workspace) -> VamlaParams:
-    torch = _torch()
-    for t, nm in ((cu_prefix, "cu_prefix"), (cu_tree, "cu_tree")):
-        if t.dtype != torch.int32:
-            raise TypeError(f"{nm} must be int32")
+    _index(cu_prefix, prob.batch + 1, "cu_prefix")
+    _index(cu_tree, prob.batch + 1, "cu_tree")
     return prob.params(_ptr(cu_prefix), _ptr(cu_tree), ws.ptr, ws.nbytes)
+
+
+# Shape and dtype checks: the kernels trust every size they are given, so a
+# wrong dtype (an int64 index tensor read as int32 pairs) or a short output
+# buffer would be read or written past its end.  These run before any launch.
+
+def _index(t, min_numel: int, what: str) -> None:
+    torch = _torch()
+    if t is None:
+        raise ValueError(f"{what} is required")
+    if t.dtype != torch.int32:
+        raise TypeError(f"{what} must be int32, got {t.dtype}")
+    if t.numel() < min_numel:
+        raise ValueError(f"{what} has {t.numel()} elements, needs at least {min_numel}")
+
+
+def _shaped(t, shape, dtypes, what: str) -> None:
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{what} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{what} must be {' or '.join(str(d) for d in dtypes)}, got {t.dtype}")
+
+
+def _bf16_like():
+    torch = _torch()
+    return (torch.bfloat16, torch.int16, torch.uint16)
+
+
+def _check_pool(kv_pool, pool_slots: int) -> None:
+    if kv_pool.dim() != 2 or kv_pool.shape[1] != D_QK:
+        raise ValueError(f"kv_pool must have shape [P, {D_QK}], got {tuple(kv_pool.shape)}")
+    if kv_pool.dtype not in _bf16_like():
+        raise TypeError(f"kv_pool must be bfloat16, got {kv_pool.dtype}")
+    if kv_pool.shape[0] < pool_slots:
+        raise ValueError(f"kv_pool has {kv_pool.shape[0]} rows, pool_slots says {pool_slots}")
+
+
+def _check_inputs(prob: Problem, q, kv_pool, prefix_slot_idx, tree_slot_idx, parent, cu_prefix, cu_tree) -> None:
+    T, H = prob.total_tree, prob.num_heads
+    _index(cu_prefix, prob.batch + 1, "cu_prefix")
+    _index(cu_tree, prob.batch + 1, "cu_tree")
+    _shaped(q, (T, H, D_QK), _bf16_like(), "q")
+    _check_pool(kv_pool, prob.pool_slots)
+    if prob.total_prefix:
+        _index(prefix_slot_idx, prob.total_prefix, "prefix_slot_idx")
+    _index(tree_slot_idx, T, "tree_slot_idx")
+    _index(parent, T, "parent")
+
+
+def _check_outputs(prob: Problem, out, lse) -> None:
+    torch = _torch()
+    T, H = prob.total_tree, prob.num_heads
+    _shaped(out, (T, H, D_V), (torch.bfloat16,), "out")
+    _shaped(lse, (T, H), (torch.float32,), "lse")
 
 
 def verify_attn_mla(prob: Problem, q, kv_pool, prefix_slot_idx, tree_slot_idx, parent, cu_prefix, cu_tree,
                     ws: Optional[Workspace] = None, out=None, lse=None, stream=None) -> Tuple[object, object]:
     """out [T, H, 512] bf16, lse [T, H] fp32 for every tree node and head."""
     torch = _torch()
-    ws = ws or Workspace(prob, q.device)
+    _check_inputs(prob, q, kv_pool, prefix_slot_idx, tree_slot_idx, parent, cu_prefix, cu_tree)
     T, H = prob.total_tree, prob.num_heads
     if out is None:
         out = torch.empty((T, H, D_V), dtype=torch.bfloat16, device=q.device)
     if lse is None:
         lse = torch.empty((T, H), dtype=torch.float32, device=q.device)
+    _check_outputs(prob, out, lse)
+    ws = ws or Workspace(prob, q.device)
     p = _params(prob, cu_prefix, cu_tree, ws)
     st = lib().verify_attn_mla(ctypes.byref(p), _ptr(_bits(q, "q")), _ptr(_bits(kv_pool, "kv_pool")),
                                _ptr(prefix_slot_idx) if prob.total_prefix else None, _ptr(tree_slot_idx),
@@ -261,6 +319,7 @@ def split_partials(prob: Problem, q, kv_pool, prefix_slot_idx, tree_slot_idx, pa
                    ws: Workspace, stream=None):
     """Stage 1: chunk partials into the workspace (the last chunk of each
     request also covers its tree keys)."""
+    _check_inputs(prob, q, kv_pool, prefix_slot_idx, tree_slot_idx, parent, cu_prefix, cu_tree)
     p = _params(prob, cu_prefix, cu_tree, ws)
     _check(lib().vamla_split_partials(ctypes.byref(p), _ptr(_bits(q, "q")), _ptr(_bits(kv_pool, "kv_pool")),
                                       _ptr(prefix_slot_idx) if prob.total_prefix else None, _ptr(tree_slot_idx),
@@ -268,6 +327,7 @@ def split_partials(prob: Problem, q, kv_pool, prefix_slot_idx, tree_slot_idx, pa
 
 
 def lse_merge(prob: Problem, cu_prefix, cu_tree, ws: Workspace, out, lse, stream=None):
+    _check_outputs(prob, out, lse)
     p = _params(prob, cu_prefix, cu_tree, ws)
     _check(lib().vamla_lse_merge(ctypes.byref(p), _ptr(out), _ptr(lse), _stream(stream)), "vamla_lse_merge")
 
@@ -275,9 +335,13 @@ def lse_merge(prob: Problem, cu_prefix, cu_tree, ws: Workspace, out, lse, stream
 def slot_gather(kv_pool, idx, dst=None, stream=None):
     """dst[l] = kv_pool[idx[l]] (bit-exact)."""
     torch = _torch()
+    _index(idx, 0, "idx")
+    if kv_pool.dim() != 2 or kv_pool.shape[1] != D_QK or kv_pool.dtype not in _bf16_like():
+        raise ValueError(f"kv_pool must be bfloat16 [P, {D_QK}], got {kv_pool.dtype} {tuple(kv_pool.shape)}")
     n = idx.numel()
     if dst is None:
         dst = torch.empty((n, D_QK), dtype=kv_pool.dtype, device=kv_pool.device)
+    _shaped(dst, (n, D_QK), _bf16_like(), "dst")
     _check(lib().vamla_slot_gather(_ptr(_bits(kv_pool, "kv_pool")), _ptr(idx) if n else None, n,
                                    _ptr(dst) if n else None, _stream(stream)), "vamla_slot_gather")
     return dst
@@ -300,3 +364,15 @@ def workspace_views(prob: Problem, ws: Workspace):
     return dict(plan=info,
                 part_o=region(info.off_part_o, (B, R, C, D_V // 4, ROW_TILE, 4)),
                 part_lse=region(info.off_part_lse, (B, R, C, ROW_TILE)))
+
+
+def debug_record(prob: Problem, ws: Workspace, with_restarts: bool = False):
+    """The device-side check's record (VAMLA_FLAG_DEBUG_VALIDATE) as a host
+    tuple (status, array, index); (0, 0, 0) when the index data was valid.
+    with_restarts appends the split pass's restart count.  Reads the
+    workspace after the caller's stream has finished the call."""
+    torch = _torch()
+    info = plan(prob)
+    off = info.off_debug_record
+    rec = ws.buf[off:off + 16].view(torch.int32).cpu().tolist()
+    return (rec[0], rec[1], rec[2], rec[3]) if with_restarts else (rec[0], rec[1], rec[2])

@@ -38,6 +38,7 @@ struct PrefixArgs {
   int32_t total_tree;         // the request's bounds from these two, not cu_*
   float scale_log2;           // softmax_scale * log2(e)
   int32_t device_lengths;     // 1: lengths from cu_* only, chunk from device_chunk()
+  const int32_t* debug_record; // non-null with VAMLA_FLAG_DEBUG_VALIDATE: no work if record[0] != 0
 };
 
 // LSE merge of the chunk partials.
@@ -58,6 +59,24 @@ struct MergeArgs {
   int32_t row_bits;           // log2 of the rows a wave covers (<= 6): live rows of a tile, rounded up
   int32_t chunk_wave_bits;    // log2 of the waves that split one column group's chunks (<= 2)
   int32_t device_lengths;     // as in PrefixArgs
+  const int32_t* debug_record; // as in PrefixArgs; a set record makes the merge write NaN
+};
+
+// Device-side check of the index arrays (VAMLA_FLAG_DEBUG_VALIDATE).
+struct ValidateArgs {
+  const int32_t* cu_prefix;
+  const int32_t* cu_tree;
+  const int32_t* parent;
+  const int32_t* prefix_slot;
+  const int32_t* tree_slot;
+  int32_t* record;            // int32[4]: status, array, index, 0 (all zero: valid)
+  int64_t max_prefix;
+  int64_t total_prefix;
+  int64_t pool_slots;
+  int32_t batch;
+  int32_t max_tree;
+  int32_t total_tree;
+  int32_t device_lengths;
 };
 
 // Chunk size chosen on the device from the longest prefix in cu_prefix: the
@@ -78,6 +97,7 @@ __device__ __forceinline__ int device_chunk(const int32_t* cu_prefix, int batch,
 
 hipError_t launch_prefix_splitkv(const PrefixArgs& a, hipStream_t stream);
 hipError_t launch_lse_merge(const MergeArgs& a, hipStream_t stream);
+hipError_t launch_debug_validate(const ValidateArgs& a, hipStream_t stream);
 hipError_t launch_slot_gather(const uint16_t* pool, const int32_t* idx, int64_t n, uint16_t* dst,
                               hipStream_t stream);
 

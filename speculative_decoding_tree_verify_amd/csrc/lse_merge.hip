@@ -64,6 +64,17 @@ __device__ __forceinline__ State shfl_state(const State& x, int mask) {
 
 __global__ __launch_bounds__(64 * kWaves) void lse_merge_kernel(MergeArgs a) {
   __shared__ State red[kWaves][kRowTile];
+  if (a.debug_record && __builtin_amdgcn_readfirstlane(a.debug_record[0]) != 0) {
+    // the index data failed the device-side check: every output is NaN (the
+    // lengths may be what failed, so rows are covered by the call's totals)
+    const int64_t rows = (int64_t)a.total_tree * a.num_heads;
+    const int64_t nthreads = (int64_t)gridDim.x * gridDim.y * blockDim.x;
+    const int64_t gid = ((int64_t)blockIdx.y * gridDim.x + blockIdx.x) * blockDim.x + threadIdx.x;
+    const uint2 nan2 = make_uint2(0x7FC07FC0u, 0x7FC07FC0u);
+    for (int64_t i = gid; i < rows * (kDv / 4); i += nthreads) *(uint2*)(a.out + i * 4) = nan2;
+    for (int64_t i = gid; i < rows; i += nthreads) a.lse[i] = __builtin_nanf("");
+    return;
+  }
   const int item = blockIdx.x;
   const int b = item / a.row_tiles;
   const int tile = item - b * a.row_tiles;

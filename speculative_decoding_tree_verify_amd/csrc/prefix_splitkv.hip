@@ -59,10 +59,15 @@
 // running max, so the accumulators are never rescaled.  The first tile sets m
 // to the row's max over that tile (the two QK waves of a row pair exchange
 // their halves through LDS at the first barrier).  While every score stays within kSlack of
-// m, exp2(s - m) <= 2^kSlack, far inside bf16/fp32 range.  A tile that breaks
-// this (rare) makes the workgroup restart its item with m raised to that
-// tile's max plus kSlack; each restart needs a new, larger tile max, so there
-// are at most as many restarts as tiles.
+// m, exp2(s - m) <= 2^kSlack, inside bf16/fp32 range (the accumulators overflow
+// only if |V| * keys of a chunk reached 2^(128 - kSlack)).  A tile that breaks
+// this (a jump of more than 27 nats: rare) makes the workgroup restart its
+// item with each row's m raised to max(m, the row's max over that tile): rows
+// that did not break keep a reference at or below their true max, so no row's
+// exponentials drift towards underflow however many restarts there are; each
+// restart needs a new tile max more than kSlack above a reference, so there
+// are at most as many restarts as tiles.  With the debug flag the kernel adds
+// its restarts to a counter in the debug record.
 
 #include "kernels.h"
 
@@ -78,7 +83,7 @@ typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 constexpr float kLn2 = 0.69314718055994530942f;
-constexpr float kSlack = 16.0f;
+constexpr float kSlack = 40.0f;
 constexpr int kKT = 32;                       // keys per tile
 constexpr int kTileLds = kKT * kDqk * 2;      // 36864 B
 constexpr int kRopeOff = kKT * 1024;          // rope parts after the 32 latent rows
@@ -231,6 +236,8 @@ __global__ __launch_bounds__(512, 1) void prefix_splitkv_kernel(PrefixArgs a) {
   static_assert(kRing == 4, "ring slots are picked by the low two bits of the tile index");
   auto ring = [&](int i) -> uint8_t* { i &= kRing - 1; return i == 0 ? tile0 : i == 1 ? tile1 : i == 2 ? tile2 : tile3; };
 
+  // with the debug flag, a failed device-side index check leaves no work
+  if (a.debug_record && __builtin_amdgcn_readfirstlane(a.debug_record[0]) != 0) return;
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const bool is_qk = w < 4;
@@ -367,6 +374,7 @@ __global__ __launch_bounds__(512, 1) void prefix_splitkv_kernel(PrefixArgs a) {
     float lsum[2] = {0.f, 0.f};
     bool have_ref = false;
     int restart_tile = 0;
+    int restarts = 0;
     // max of row 16nb + l16 of the pair over tile slot k: its four lanes in
     // this wave and in the partner wave
     auto pair_row_max = [&](int k, int nb) {
@@ -502,16 +510,19 @@ __global__ __launch_bounds__(512, 1) void prefix_splitkv_kernel(PrefixArgs a) {
         lds_barrier();
       }
       if (!restart) break;
-      // restart with the pair's max over the offending tile plus headroom
+      ++restarts;
+      // restart with each row's reference raised to its max over the offending tile
       const int bad = restart_tile % 3;
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) {
-        m_ref[nb] = fmaxf(m_ref[nb], pair_row_max(bad, nb)) + kSlack;
+        m_ref[nb] = fmaxf(m_ref[nb], pair_row_max(bad, nb));
         lsum[nb] = 0.f;
       }
       have_ref = true;
       __syncthreads();
     }
+    if (a.debug_record && restarts > 0 && w == 0 && lane == 0)
+      atomicAdd(const_cast<int32_t*>(a.debug_record) + 3, restarts);
     // row sums: the four lanes of the row, then the partner wave
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) lsum[nb] = sum4(lsum[nb]);

@@ -42,7 +42,7 @@ int check_shape(const vamla_params* p) {
   if (!p) return VAMLA_ERR_INVALID_ARG;
   if (p->batch < 1 || p->pool_slots < 1 || p->max_prefix < 0 || p->total_prefix < 0 || p->total_tree < 1)
     return VAMLA_ERR_INVALID_ARG;
-  if ((p->flags & ~VAMLA_FLAG_DEVICE_LENGTHS) != 0) return VAMLA_ERR_INVALID_ARG;
+  if ((p->flags & ~(VAMLA_FLAG_DEVICE_LENGTHS | VAMLA_FLAG_DEBUG_VALIDATE)) != 0) return VAMLA_ERR_INVALID_ARG;
   if (!(std::isfinite(p->softmax_scale) && p->softmax_scale > 0.f)) return VAMLA_ERR_INVALID_ARG;
   if (p->d_qk != VAMLA_D_QK || p->d_v != VAMLA_D_V) return VAMLA_ERR_UNSUPPORTED;
   if (p->num_heads < 1 || p->num_heads > VAMLA_MAX_HEADS) return VAMLA_ERR_UNSUPPORTED;
@@ -53,6 +53,10 @@ int check_shape(const vamla_params* p) {
     return VAMLA_ERR_UNSUPPORTED;
   if ((int64_t)p->total_tree * p->num_heads > (int64_t)INT32_MAX / VAMLA_D_V) return VAMLA_ERR_UNSUPPORTED;
   if (p->pool_slots > (int64_t)UINT32_MAX) return VAMLA_ERR_UNSUPPORTED;
+  // the totals must fit the planning bounds: chunks and row tiles are sized
+  // from max_prefix / max_tree, so a longer request would be cut short
+  if (p->total_prefix > (int64_t)p->batch * p->max_prefix) return VAMLA_ERR_INVALID_ARG;
+  if ((int64_t)p->total_tree > (int64_t)p->batch * p->max_tree) return VAMLA_ERR_INVALID_ARG;
   return VAMLA_OK;
 }
 
@@ -113,6 +117,8 @@ int make_plan(const vamla_params* p, vamla_plan_info* out) {
   off = align256(off + (size_t)items * item_o);
   pl.off_part_lse = off;
   off = align256(off + (size_t)items * item_l);
+  pl.off_debug_record = off;
+  off = align256(off + 4 * sizeof(int32_t));
   pl.workspace_bytes = off;
   *out = pl;
   return VAMLA_OK;
@@ -142,6 +148,29 @@ int workspace_ok(const vamla_params* p, const vamla_plan_info& pl) {
 
 float* ws_f(const vamla_params* p, size_t off) { return (float*)((char*)p->workspace + off); }
 
+int32_t* debug_record(const vamla_params* p, const vamla_plan_info& pl) {
+  return (p->flags & VAMLA_FLAG_DEBUG_VALIDATE) ? (int32_t*)((char*)p->workspace + pl.off_debug_record) : nullptr;
+}
+
+int validate_launch(const vamla_params* p, const vamla_plan_info& pl, const int32_t* prefix_slot_idx,
+                    const int32_t* tree_slot_idx, const int32_t* parent, hipStream_t stream) {
+  ValidateArgs a;
+  a.cu_prefix = p->cu_prefix;
+  a.cu_tree = p->cu_tree;
+  a.parent = parent;
+  a.prefix_slot = prefix_slot_idx;
+  a.tree_slot = tree_slot_idx;
+  a.record = debug_record(p, pl);
+  a.max_prefix = p->max_prefix;
+  a.total_prefix = p->total_prefix;
+  a.pool_slots = p->pool_slots;
+  a.batch = p->batch;
+  a.max_tree = p->max_tree;
+  a.total_tree = p->total_tree;
+  a.device_lengths = (p->flags & VAMLA_FLAG_DEVICE_LENGTHS) ? 1 : 0;
+  return launch_debug_validate(a, stream) == hipSuccess ? VAMLA_OK : VAMLA_ERR_LAUNCH;
+}
+
 int split_launch(const vamla_params* p, const vamla_plan_info& pl, const uint16_t* q, const uint16_t* pool,
                  const int32_t* prefix_slot_idx, const int32_t* tree_slot_idx, const int32_t* parent,
                  hipStream_t stream) {
@@ -165,6 +194,11 @@ int split_launch(const vamla_params* p, const vamla_plan_info& pl, const uint16_
   a.total_tree = p->total_tree;
   a.scale_log2 = p->softmax_scale * 1.4426950408889634f;
   a.device_lengths = (p->flags & VAMLA_FLAG_DEVICE_LENGTHS) ? 1 : 0;
+  a.debug_record = debug_record(p, pl);
+  if (a.debug_record) {
+    const int st = validate_launch(p, pl, prefix_slot_idx, tree_slot_idx, parent, stream);
+    if (st != VAMLA_OK) return st;
+  }
   return launch_prefix_splitkv(a, stream) == hipSuccess ? VAMLA_OK : VAMLA_ERR_LAUNCH;
 }
 
@@ -184,6 +218,7 @@ int merge_launch(const vamla_params* p, const vamla_plan_info& pl, uint16_t* out
   a.total_prefix = (int32_t)p->total_prefix;
   a.total_tree = p->total_tree;
   a.device_lengths = (p->flags & VAMLA_FLAG_DEVICE_LENGTHS) ? 1 : 0;
+  a.debug_record = debug_record(p, pl);
   // a wave covers the live rows of a tile (at most max_tree * H when there is
   // one row tile), its other lanes split the chunks
   const int64_t tile_rows = std::min<int64_t>(kRowTile, (int64_t)p->max_tree * p->num_heads);

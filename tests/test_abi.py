@@ -222,22 +222,101 @@ def test_validate_catches_bad_slots_and_lengths(L):
     cp[1] += 1
     assert vb.validate(p, x.parent, x.cu_tree, cp) == -8
     p2 = vb.Problem(**{**p.__dict__, "max_tree": 8})
-    assert vb.validate(p2, x.parent, x.cu_tree, x.cu_prefix) == -8
+    assert vb.validate(p2, x.parent, x.cu_tree, x.cu_prefix) == -1     # total_tree > batch * max_tree
+    # two requests within the totals' bound, one of them past max_tree
+    x2 = gen.make_inputs([10, 10], [gen.random_tree(3, np.random.default_rng(2)),
+                                    gen.random_tree(7, np.random.default_rng(3))], 2, 64, "scrambled", seed=4)
+    p3 = vb.Problem.from_host(x2.cu_prefix, x2.cu_tree, 2, 64, 0.1)
+    assert vb.validate(p3, x2.parent, x2.cu_tree, x2.cu_prefix, x2.prefix_slot_idx, x2.tree_slot_idx) == 0
+    p3.max_tree = 5
+    assert vb.validate(p3, x2.parent, x2.cu_tree, x2.cu_prefix) == -8
 
 
 def test_flags(L):
-    # only VAMLA_FLAG_DEVICE_LENGTHS is defined; it does not change the plan
+    # VAMLA_FLAG_DEVICE_LENGTHS and VAMLA_FLAG_DEBUG_VALIDATE are defined; neither changes the plan
     p = prob(3)
     base = vb.plan(p)
-    p.flags = vb.FLAG_DEVICE_LENGTHS
-    info = vb.plan(p)
-    assert (info.chunk, info.max_chunks, info.grid_items, info.workspace_bytes) == \
-        (base.chunk, base.max_chunks, base.grid_items, base.workspace_bytes)
-    for bad in (2, 4, 1 << 31, 3):
+    for ok in (vb.FLAG_DEVICE_LENGTHS, vb.FLAG_DEBUG_VALIDATE, vb.FLAG_DEVICE_LENGTHS | vb.FLAG_DEBUG_VALIDATE):
+        p.flags = ok
+        info = vb.plan(p)
+        assert (info.chunk, info.max_chunks, info.grid_items, info.workspace_bytes, info.off_debug_record) == \
+            (base.chunk, base.max_chunks, base.grid_items, base.workspace_bytes, base.off_debug_record)
+    for bad in (4, 8, 1 << 31, 7):
         p.flags = bad
         with pytest.raises(vb.VamlaError) as e:
             vb.plan(p)
         assert e.value.status == -1
+
+
+def test_debug_record_sits_inside_the_workspace(L):
+    for k in range(1, 8):
+        info = vb.plan(prob(k))
+        assert info.off_debug_record % 256 == 0
+        assert info.off_debug_record >= info.off_part_lse
+        assert info.off_debug_record + 16 <= info.workspace_bytes
+
+
+@pytest.mark.parametrize("batch,max_tree,total_tree,max_prefix,total_prefix", [
+    (1, 4, 9, 100, 100),        # one request with more nodes than max_tree
+    (1, 9, 9, 0, 1000),         # one request with a prefix past max_prefix
+    (3, 9, 28, 100, 200),       # more nodes in total than 3 requests of max_tree
+    (3, 9, 27, 100, 301),       # more prefix in total than 3 requests of max_prefix
+])
+def test_plan_rejects_totals_beyond_the_bounds(L, batch, max_tree, total_tree, max_prefix, total_prefix):
+    # chunks and row tiles are planned from the bounds: a request past them
+    # would be cut short silently
+    p = vb.Problem(batch, 16, 1 << 20, gen.SOFTMAX_SCALE, max_tree, total_tree, max_prefix, total_prefix)
+    with pytest.raises(vb.VamlaError) as e:
+        vb.plan(p)
+    assert e.value.status == -1
+    p.total_tree, p.total_prefix = min(total_tree, batch * max_tree), min(total_prefix, batch * max_prefix)
+    vb.plan(p)
+
+
+def test_binding_checks_arguments_before_any_launch(L):
+    # wrong dtypes and sizes raise in the binding (CPU tensors: the checks
+    # come before the device-pointer check, so nothing reaches the library)
+    import torch
+    x, p = _valid_case()
+    T, H = x.total_tree, x.num_heads
+    ok = dict(q=torch.zeros((T, H, 576), dtype=torch.bfloat16),
+              kv_pool=torch.zeros((x.pool.shape[0], 576), dtype=torch.bfloat16),
+              prefix_slot_idx=torch.zeros(x.total_prefix, dtype=torch.int32),
+              tree_slot_idx=torch.zeros(T, dtype=torch.int32), parent=torch.zeros(T, dtype=torch.int32),
+              cu_prefix=torch.tensor(x.cu_prefix), cu_tree=torch.tensor(x.cu_tree))
+    out_ok = torch.zeros((T, H, 512), dtype=torch.bfloat16)
+    lse_ok = torch.zeros((T, H), dtype=torch.float32)
+
+    def call(**kw):
+        a = dict(ok, **{k: v for k, v in kw.items() if k in ok})
+        return vb.verify_attn_mla(p, a["q"], a["kv_pool"], a["prefix_slot_idx"], a["tree_slot_idx"], a["parent"],
+                                  a["cu_prefix"], a["cu_tree"], out=kw.get("out", out_ok), lse=kw.get("lse", lse_ok))
+    bad_cases = [
+        dict(prefix_slot_idx=torch.zeros(x.total_prefix, dtype=torch.int64)),      # int64 read as int32 pairs
+        dict(prefix_slot_idx=torch.zeros(x.total_prefix - 1, dtype=torch.int32)),  # short
+        dict(tree_slot_idx=torch.zeros(T - 1, dtype=torch.int32)),
+        dict(parent=torch.zeros(T, dtype=torch.int64)),
+        dict(cu_prefix=torch.tensor(x.cu_prefix, dtype=torch.int64)),
+        dict(cu_tree=torch.zeros(1, dtype=torch.int32)),
+        dict(q=torch.zeros((T, H, 512), dtype=torch.bfloat16)),
+        dict(q=torch.zeros((T, H, 576), dtype=torch.float32)),
+        dict(kv_pool=torch.zeros((x.pool.shape[0] - 1, 576), dtype=torch.bfloat16)),  # fewer rows than pool_slots
+        dict(kv_pool=torch.zeros((x.pool.shape[0], 512), dtype=torch.bfloat16)),
+        dict(out=torch.zeros((T, H, 512), dtype=torch.float32)),
+        dict(out=torch.zeros((T - 1, H, 512), dtype=torch.bfloat16)),
+        dict(lse=torch.zeros((T, H), dtype=torch.bfloat16)),
+        dict(lse=torch.zeros((T, H + 1), dtype=torch.float32)),
+    ]
+    for kw in bad_cases:
+        with pytest.raises((TypeError, ValueError)) as e:
+            call(**kw)
+        assert "GPU" not in str(e.value), (kw, e.value)      # refused by a shape/dtype check
+    with pytest.raises(ValueError, match="GPU"):                # well-formed CPU tensors reach the device check
+        call()
+    with pytest.raises((TypeError, ValueError)):
+        vb.slot_gather(ok["kv_pool"], torch.zeros(4, dtype=torch.int64))
+    with pytest.raises((TypeError, ValueError)):
+        vb.slot_gather(ok["kv_pool"], torch.zeros(4, dtype=torch.int32), dst=torch.zeros((3, 576), dtype=torch.bfloat16))
 
 
 def test_bench_refuses_more_than_one_gpu():

@@ -137,3 +137,52 @@ def test_one_capture_serves_changing_prefix_lengths(cap, variants):
         assert_close_lse(lse_g.cpu().numpy().astype(np.float64), rl, f"lengths {lens}")
         assert_close_out(out_g.float().cpu().numpy().astype(np.float64), ro, f"lengths {lens}")
         log(f"[case] lengths {lens}: replay matches eager bit for bit and the oracle")
+
+
+def test_full_size_capture_replayed_at_shorter_prefixes():
+    # one graph captured for the 64k-prefix / 65-node workload with lengths
+    # read on the device, replayed with the prefix cut to 40000 and 12345
+    # keys: the kernels pick a smaller chunk than the host plan and must
+    # still match an eager call bit for bit and the oracle (sampled heads)
+    import torch
+    x = gen.config_inputs(3)
+    d = to_dev(x)
+    p = problem(x)
+    p.flags = vb.FLAG_DEVICE_LENGTHS
+    ws_g, ws_e = vb.Workspace(p), vb.Workspace(p)
+    T, H = x.total_tree, x.num_heads
+    out_g = torch.empty((T, H, 512), dtype=torch.bfloat16, device="cuda")
+    lse_g = torch.empty((T, H), dtype=torch.float32, device="cuda")
+
+    def step():
+        vb.verify_attn_mla(p, d["q"], d["kv_pool"], d["prefix_slot_idx"], d["tree_slot_idx"], d["parent"],
+                           d["cu_prefix"], d["cu_tree"], ws=ws_g, out=out_g, lse=lse_g)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    for L in (40000, 12345):
+        log(f"[case] 64k capture replayed at prefix {L}")
+        d["cu_prefix"].copy_(torch.tensor([0, L], dtype=torch.int32))
+        out_g.fill_(float("nan"))
+        lse_g.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        ref_out, ref_lse = _eager(p, d, ws_e)
+        assert torch.equal(out_g.view(torch.int16), ref_out.view(torch.int16)), f"prefix {L}: replay differs"
+        assert torch.equal(lse_g, ref_lse), f"prefix {L}: replay lse differs"
+        heads = [1, 8, 14]
+        ro, rl = vo.verify(x.q, x.pool, x.prefix_slot_idx[:L], x.tree_slot_idx, x.parent,
+                           np.array([0, L], np.int32), x.cu_tree, x.scale, heads=heads)
+        got_l = lse_g.cpu().numpy().astype(np.float64)[:, heads]
+        got_o = out_g.float().cpu().numpy().astype(np.float64)[:, heads]
+        assert_close_lse(got_l, rl[:, heads], f"prefix {L}")
+        assert_close_out(got_o, ro[:, heads], f"prefix {L}")

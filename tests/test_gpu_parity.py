@@ -145,9 +145,51 @@ def test_reference_jump_mid_chunk(chunk, H, N, node, head):
     key = 1500
     slot = x.prefix_slot_idx[key]
     k = vo.bf16_bits_to_f64(x.pool[slot])
-    x.q[node, head] = gen.f32_to_bf16_bits((k * 40.0).astype(np.float32))            # score ~ 40*|k|^2*sigma
-    out, lse = check(x, chunk=chunk, what=f"reference jump chunk={chunk} rows={H * N} node={node} head={head}")
+    # score ~ 100*|k|^2*sigma ~ 42 nats above the rest: past the split kernel's
+    # 2^40 headroom, so with 2048-key chunks the chunk restarts
+    x.q[node, head] = gen.f32_to_bf16_bits((k * 100.0).astype(np.float32))
+    out, lse, restarts = check_debug(x, chunk, f"reference jump chunk={chunk} rows={H * N} node={node} head={head}")
     np.testing.assert_allclose(out[node, head], k[:512], atol=2e-2)
+    if chunk == 2048:
+        assert restarts >= 1
+
+
+def check_debug(x, chunk, what):
+    """check() through a call with VAMLA_FLAG_DEBUG_VALIDATE; also returns the
+    split pass's restart count."""
+    import torch
+    log(f"[case] {what} (debug record)")
+    p = problem(x, chunk)
+    p.flags = vb.FLAG_DEBUG_VALIDATE
+    d = to_dev(x)
+    ws = vb.Workspace(p)
+    o, l = vb.verify_attn_mla(p, d["q"], d["kv_pool"], d["prefix_slot_idx"], d["tree_slot_idx"], d["parent"],
+                              d["cu_prefix"], d["cu_tree"], ws=ws)
+    torch.cuda.synchronize()
+    rec = vb.debug_record(p, ws, with_restarts=True)
+    assert rec[:3] == (0, 0, 0)
+    out, lse = o.float().cpu().numpy().astype(np.float64), l.cpu().numpy().astype(np.float64)
+    ro, rl = oracle_full(x)
+    assert_close_lse(lse, rl, what)
+    assert_close_out(out, ro, what)
+    return out, lse, rec[3]
+
+
+def test_repeated_restarts_leave_other_rows_exact():
+    # one row meets four keys whose scores climb by ~42 nats each inside one
+    # 2048-key chunk: four restarts of the chunk.  Every other row of the tile
+    # (same row pair included) keeps a reference at or below its own max, so
+    # all rows still match the oracle, and the climbing row ends on the last key
+    rng = np.random.default_rng(70)
+    H, N, node, head = 4, 9, 3, 2
+    x = small([2000], [gen.random_tree(N, rng)], H, seed=71)
+    k = vo.bf16_bits_to_f64(x.pool[x.prefix_slot_idx[100]])
+    x.q[node, head] = gen.f32_to_bf16_bits((k * 100.0).astype(np.float32))
+    for g, pos in enumerate((300, 700, 1100, 1500), start=1):
+        x.pool[x.prefix_slot_idx[pos]] = gen.f32_to_bf16_bits((k * g).astype(np.float32))
+    out, lse, restarts = check_debug(x, 2048, "four climbing keys in one chunk")
+    assert restarts >= 4
+    np.testing.assert_allclose(out[node, head], 4 * k[:512], atol=4e-2)
 
 
 def test_config1():
@@ -167,6 +209,43 @@ def test_config3_full():
     check(x, what="config 3")
 
 
+def test_config3_lengths_on_the_device():
+    # the chunk size is chosen in the kernels from cu_prefix (the 65536-key
+    # prefix over the plan's chunk slots), not taken from the host plan
+    x = gen.config_inputs(3)
+    info = vb.plan(problem(x))
+    dev_chunk = max(32, -(-(-(-65536 // info.max_chunks)) // 32) * 32)
+    log(f"config 3 host chunk {info.chunk}, device chunk {dev_chunk}, {info.max_chunks} chunk slots")
+    check(x, heads=[0, 6, 15], what="config 3, lengths on the device", flags=vb.FLAG_DEVICE_LENGTHS)
+
+
+def test_config3_planted_tree_keys():
+    # at full size one wrong tree key moves lse by ~1/65601, far below the
+    # lse bound; a planted key makes the mask visible: a node whose query is
+    # a large multiple of an ancestor's key must output that key's V row,
+    # one planted on a key it must not see must not
+    x = gen.config_inputs(3)
+    par = x.parent
+    depth = gen.tree_depths(par)
+    deep = [int(t) for t in np.argsort(-depth)[:3]]
+    planted = {}
+    for i, t in enumerate(deep):
+        anc = vo.ancestors_or_self(par, t)
+        j = anc[len(anc) // 2]                       # a visible ancestor, not the node itself
+        hidden = next(u for u in range(len(par)) if u not in anc)
+        h_vis, h_hid = (3 * i) % 16, (3 * i + 7) % 16
+        kv = vo.bf16_bits_to_f64(x.pool[x.tree_slot_idx[j]])
+        kh = vo.bf16_bits_to_f64(x.pool[x.tree_slot_idx[hidden]])
+        x.q[t, h_vis] = gen.f32_to_bf16_bits((kv * 40.0).astype(np.float32))
+        x.q[t, h_hid] = gen.f32_to_bf16_bits((kh * 40.0).astype(np.float32))
+        planted[t] = (h_vis, kv, h_hid, kh)
+    heads = sorted({h for v in planted.values() for h in (v[0], v[2])})
+    out, lse = check(x, heads=heads, what="config 3, planted tree keys")
+    for t, (h_vis, kv, h_hid, kh) in planted.items():
+        np.testing.assert_allclose(out[t, h_vis], kv[:512], atol=2e-2)
+        assert np.abs(out[t, h_hid] - kh[:512]).max() > 0.1
+
+
 def test_config4_sampled_heads():
     x = gen.config_inputs(4)
     check(x, heads=[0, 77, 127], what="config 4 heads 0,77,127")
@@ -176,6 +255,12 @@ def test_config5_sampled_requests():
     x = gen.config_inputs(5)
     log(f"config 5 prefix lengths {[x.prefix_len(b) for b in range(8)]}")
     check(x, requests=[0, 3, 7], heads=[0, 9, 15], what="config 5 requests 0,3,7")
+
+
+def test_config5_other_requests():
+    # every request of the batch meets the oracle: 1, 2, 4, 5, 6 on two heads each
+    x = gen.config_inputs(5)
+    check(x, requests=[1, 2, 4, 5, 6], heads=[4, 11], what="config 5 requests 1,2,4,5,6")
 
 
 def test_small_rows_decode_full():

@@ -222,6 +222,67 @@ def test_prefix_and_tree_partials_merge_to_verify():
     np.testing.assert_allclose(mo.reshape(out.shape), out, rtol=0, atol=1e-12)
 
 
+def _batch_case(lens, parents, H, seed):
+    """Several requests sharing one NaN-poisoned pool (full 576/512 dims)."""
+    rng = np.random.default_rng(seed)
+    Ns = [len(p) for p in parents]
+    need = sum(lens) + sum(Ns)
+    P = need + 9
+    slots = rng.permutation(np.arange(1, P))[:need]
+    pool = np.full((P, 576), 0x7FC0, dtype=np.uint16)
+    pool[slots] = _bf16(rng.standard_normal((need, 576)) * 0.7)
+    T = sum(Ns)
+    return dict(q_bits=_bf16(rng.standard_normal((T, H, 576)) * 0.7), pool_bits=pool,
+                prefix_slot_idx=slots[:sum(lens)].astype(np.int32), tree_slot_idx=slots[sum(lens):].astype(np.int32),
+                parent=np.concatenate([np.asarray(p, np.int32) for p in parents]),
+                cu_prefix=np.concatenate([[0], np.cumsum(lens)]).astype(np.int32),
+                cu_tree=np.concatenate([[0], np.cumsum(Ns)]).astype(np.int32))
+
+
+def test_partials_of_later_requests_merge_to_verify():
+    # prefix_partial / tree_partial of requests 1 and 2 read their keys and
+    # queries through cu_prefix[b] / cu_tree[b]: the merged partials of each
+    # request must equal its rows of the unsplit step (and request 0, with no
+    # prefix, its tree partial alone)
+    rng = np.random.default_rng(14)
+    parents = [gen.random_tree(4, rng), gen.random_tree(6, rng), gen.chain_plus_branch(chain=3)]
+    case = _batch_case([0, 5, 50], parents, H=2, seed=14)
+    s = gen.SOFTMAX_SCALE
+    out, lse = _run(case, s, 512)
+    assert np.isfinite(out).all() and np.isfinite(lse).all()
+    for b, cuts in enumerate([[], [(0, 2), (2, 5)], [(0, 17), (17, 50)]]):
+        t0, t1 = int(case["cu_tree"][b]), int(case["cu_tree"][b + 1])
+        args = (case["q_bits"], case["pool_bits"], case["prefix_slot_idx"], case["cu_prefix"], case["cu_tree"], b)
+        parts = [vo.prefix_partial(*args, a, e, s) for a, e in cuts]
+        parts.append(vo.tree_partial(case["q_bits"], case["pool_bits"], case["tree_slot_idx"], case["parent"],
+                                     case["cu_tree"], b, s))
+        mo, ml = vo.merge_partials([(o.reshape(-1, 512), l.reshape(-1)) for o, l in parts])
+        np.testing.assert_allclose(ml.reshape(lse[t0:t1].shape), lse[t0:t1], rtol=0, atol=1e-12)
+        np.testing.assert_allclose(mo.reshape(out[t0:t1].shape), out[t0:t1], rtol=0, atol=1e-12)
+
+
+def test_mutation_partials_ignore_request_offsets(monkeypatch):
+    # a helper that slices as if every request started at key / node 0 must
+    # fail the batched pin above
+    orig_p, orig_t = vo.prefix_partial, vo.tree_partial
+
+    def prefix_partial(q_bits, pool_bits, prefix_slot_idx, cu_prefix, cu_tree, b, k0, k1, scale, d_v=512):
+        L = int(cu_prefix[b + 1]) - int(cu_prefix[b])
+        return orig_p(q_bits, pool_bits, prefix_slot_idx, np.array([0, L]), cu_tree[b:b + 2], 0, k0, k1, scale, d_v)
+
+    def tree_partial(q_bits, pool_bits, tree_slot_idx, parent, cu_tree, b, scale, d_v=512):
+        N = int(cu_tree[b + 1]) - int(cu_tree[b])
+        return orig_t(q_bits[int(cu_tree[b]):], pool_bits, tree_slot_idx, parent, np.array([0, N]), 0, scale, d_v)
+
+    monkeypatch.setattr(vo, "prefix_partial", prefix_partial)
+    with pytest.raises(AssertionError):
+        test_partials_of_later_requests_merge_to_verify()
+    monkeypatch.setattr(vo, "prefix_partial", orig_p)
+    monkeypatch.setattr(vo, "tree_partial", tree_partial)
+    with pytest.raises(AssertionError):
+        test_partials_of_later_requests_merge_to_verify()
+
+
 def test_slot_permutation_invariance():
     rng = np.random.default_rng(8)
     parent = gen.random_tree(6, rng)
