@@ -298,10 +298,12 @@ def main():
         def verify_contiguous(i):
             vb.verify_attn_mla(prob_c, q, dst, pre_c, tre_c, par, cup, cut, ws=ws_c, out=out, lse=lse)
 
+        scattered_step = eager_step
+
         def eager_step(i):  # noqa: F811
             gather_only(i)
             verify_contiguous(i)
-        defrag = dict(gather=gather_only, verify=verify_contiguous, rows=n_rows)
+        defrag = dict(gather=gather_only, verify=verify_contiguous, rows=n_rows, scattered=scattered_step)
         wname += ", defragmented each step (slot gather + verify on the contiguous copy)"
 
     step = eager_step
@@ -375,8 +377,15 @@ def main():
     if defrag is not None:
         ms_g = time_events(defrag["gather"], iters)
         ms_v = time_after(defrag["gather"], defrag["verify"], iters)
+        # the same verify on the scattered pool, and how many steps a one-time
+        # compaction (one gather) takes to pay back
+        ms_s = time_events(defrag["scattered"], iters)
+        payback = ms_g / (ms_s - ms_v) if ms_s > ms_v else None
         defrag_us = {"slot_gather": round(ms_g * 1e3, 2), "verify_on_contiguous": round(ms_v * 1e3, 2),
-                     "rows": defrag["rows"]}
+                     "verify_on_scattered": round(ms_s * 1e3, 2),
+                     "compaction_payback_steps": round(payback, 1) if payback else None, "rows": defrag["rows"]}
+        err(f"[bench] defrag: scattered verify {ms_s * 1e3:.1f} us; one-time compaction pays back after "
+            f"{'%.1f' % payback if payback else 'never (no per-step gain)'} steps")
         err(f"[bench] defrag: slot gather of {defrag['rows']} rows {ms_g * 1e3:.1f} us "
             f"({2 * defrag['rows'] * KV_ROW_BYTES / (ms_g * 1e-3) / 1e9:.0f} GB/s read + written), "
             f"verify on the contiguous copy {ms_v * 1e3:.1f} us")
