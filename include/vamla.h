@@ -73,7 +73,9 @@ typedef enum vamla_status {
   VAMLA_ERR_LAUNCH = -5,         /* a kernel launch failed */
   VAMLA_ERR_INVALID_TREE = -6,   /* vamla_validate: parent array not topological, or not one root */
   VAMLA_ERR_INVALID_SLOT = -7,   /* vamla_validate: slot index outside [0, pool_slots) */
-  VAMLA_ERR_INVALID_LENGTHS = -8 /* vamla_validate: cumulative lengths inconsistent with params */
+  VAMLA_ERR_INVALID_LENGTHS = -8, /* vamla_validate: cumulative lengths inconsistent with params */
+  VAMLA_ERR_STATIC_LIMIT = -9     /* verify_attn_mla_static: the problem needs more workspace than
+                                     VAMLA_STATIC_WORKSPACE_BYTES */
 } vamla_status;
 
 /*
@@ -256,6 +258,27 @@ int vamla_split_partials(const vamla_params* p, const uint16_t* q, const uint16_
  * merging partial attention states by their log-sum-exp.
  */
 int vamla_lse_merge(const vamla_params* p, uint16_t* out, float* lse, void* stream);
+
+/*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the verify
+ * step of verify_attn_mla with the library's own workspace, a static device
+ * array of VAMLA_STATIC_WORKSPACE_BYTES that each GPU holds from the first
+ * such call until the process ends.  p->workspace and p->workspace_bytes are
+ * ignored; everything else is as for verify_attn_mla.  The call allocates
+ * nothing (no hipMalloc, no hipFree); its first call on a device looks up the
+ * array's device address (hipGetSymbolAddress) and keeps it.
+ * Returns VAMLA_ERR_STATIC_LIMIT, before any HIP call, when
+ * vamla_workspace_size(p) exceeds the array (about 500 work items of 64
+ * rows: e.g. 64k-token prefixes with 65 nodes and 16 heads need 33.5 MB).
+ * Calls on one GPU share the array: calls that overlap in time on one GPU
+ * (other streams, other threads) race on it and must be serialised by the
+ * caller.
+ */
+#define VAMLA_STATIC_WORKSPACE_BYTES (64u << 20)
+int verify_attn_mla_static(const vamla_params* p, const uint16_t* q, const uint16_t* kv_pool,
+                           const int32_t* prefix_slot_idx, const int32_t* tree_slot_idx,
+                           const int32_t* parent, uint16_t* out, float* lse, void* stream);
 
 /*
  * Slot compaction (defragmentation) gather: dst[l, :] = kv_pool[idx[l], :] for

@@ -29,11 +29,12 @@ FLAG_DEBUG_VALIDATE = 2
 STATUS = {
     0: "VAMLA_OK", -1: "VAMLA_ERR_INVALID_ARG", -2: "VAMLA_ERR_UNSUPPORTED", -3: "VAMLA_ERR_WORKSPACE",
     -4: "VAMLA_ERR_ARCH", -5: "VAMLA_ERR_LAUNCH", -6: "VAMLA_ERR_INVALID_TREE", -7: "VAMLA_ERR_INVALID_SLOT",
-    -8: "VAMLA_ERR_INVALID_LENGTHS",
+    -8: "VAMLA_ERR_INVALID_LENGTHS", -9: "VAMLA_ERR_STATIC_LIMIT",
 }
+STATIC_WORKSPACE_BYTES = 64 << 20
 
 EXPORTS = ("vamla_status_string", "vamla_plan", "vamla_workspace_size", "vamla_validate", "verify_attn_mla",
-           "vamla_split_partials", "vamla_lse_merge", "vamla_slot_gather")
+           "vamla_split_partials", "vamla_lse_merge", "vamla_slot_gather", "verify_attn_mla_static")
 
 
 class VamlaParams(ctypes.Structure):
@@ -98,6 +99,7 @@ def lib() -> ctypes.CDLL:
     L.vamla_split_partials.argtypes = [P(VamlaParams), vp, vp, vp, vp, vp, vp]
     L.vamla_lse_merge.argtypes = [P(VamlaParams), vp, vp, vp]
     L.vamla_slot_gather.argtypes = [vp, vp, i64, vp, vp]
+    L.verify_attn_mla_static.argtypes = [P(VamlaParams), vp, vp, vp, vp, vp, vp, vp, vp]
     for name in EXPORTS:
         if name != "vamla_status_string":
             getattr(L, name).restype = ctypes.c_int
@@ -312,6 +314,27 @@ def verify_attn_mla(prob: Problem, q, kv_pool, prefix_slot_idx, tree_slot_idx, p
                                _ptr(prefix_slot_idx) if prob.total_prefix else None, _ptr(tree_slot_idx),
                                _ptr(parent), _ptr(out), _ptr(lse), _stream(stream))
     _check(st, "verify_attn_mla")
+    return out, lse
+
+
+def verify_attn_mla_static(prob: Problem, q, kv_pool, prefix_slot_idx, tree_slot_idx, parent, cu_prefix, cu_tree,
+                           out=None, lse=None, stream=None) -> Tuple[object, object]:
+    """verify_attn_mla with the library's static device workspace (the C
+    entry point allocates nothing; out / lse are allocated here only when
+    not given)."""
+    torch = _torch()
+    _check_inputs(prob, q, kv_pool, prefix_slot_idx, tree_slot_idx, parent, cu_prefix, cu_tree)
+    T, H = prob.total_tree, prob.num_heads
+    if out is None:
+        out = torch.empty((T, H, D_V), dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty((T, H), dtype=torch.float32, device=q.device)
+    _check_outputs(prob, out, lse)
+    p = prob.params(_ptr(cu_prefix), _ptr(cu_tree))
+    st = lib().verify_attn_mla_static(ctypes.byref(p), _ptr(_bits(q, "q")), _ptr(_bits(kv_pool, "kv_pool")),
+                                      _ptr(prefix_slot_idx) if prob.total_prefix else None, _ptr(tree_slot_idx),
+                                      _ptr(parent), _ptr(out), _ptr(lse), _stream(stream))
+    _check(st, "verify_attn_mla_static")
     return out, lse
 
 

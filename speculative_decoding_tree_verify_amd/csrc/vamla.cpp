@@ -264,6 +264,7 @@ const char* vamla_status_string(int status) {
     case VAMLA_ERR_INVALID_TREE: return "invalid tree (parent array)";
     case VAMLA_ERR_INVALID_SLOT: return "slot index out of range";
     case VAMLA_ERR_INVALID_LENGTHS: return "cumulative lengths inconsistent";
+    case VAMLA_ERR_STATIC_LIMIT: return "problem needs more workspace than the static workspace holds";
     default: return "unknown status";
   }
 }

@@ -328,3 +328,13 @@ def test_bench_refuses_more_than_one_gpu():
                        text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr or "single MI355X" in r.stderr
+
+
+def test_static_entry_refuses_problems_past_its_workspace(L):
+    # 64 requests of 65 nodes x 128 heads need far more than the static
+    # workspace: refused on the host, before any HIP call (this runs without a GPU)
+    p = vb.Problem(64, 128, 1 << 20, gen.SOFTMAX_SCALE, 65, 64 * 65, 4096, 64 * 4096)
+    assert vb.workspace_size(p) > vb.STATIC_WORKSPACE_BYTES
+    prm = p.params(cu_prefix_ptr=16, cu_tree_ptr=16)
+    assert L.verify_attn_mla_static(ctypes.byref(prm), 16, 16, 16, 16, 16, 16, 16, None) == -9
+    assert L.vamla_status_string(-9) != b"unknown status"
