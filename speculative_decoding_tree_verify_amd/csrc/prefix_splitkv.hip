@@ -38,23 +38,29 @@
 // With the request lengths read on the device, the chunk size comes from
 // the longest prefix in cu_prefix (device_chunk) instead of the host plan.
 //
-// Gather: LDS-DMA moves 16 bytes per lane straight into LDS.  Latent rows: one
-// 64-lane buffer_load_dwordx4 ... lds per key with a per-row descriptor; rope
-// rows: one 64-lane global_load_lds_dwordx4 per 8 keys with 64-bit per-lane
-// addresses (buffer offsets are 32-bit, rows may lie past 4 GiB).  Both are
-// issued as asm: the compiler would otherwise make every LDS read wait for
-// them (it cannot tell the ring slots apart); the waits are explicit vmcnt
-// counts before each barrier.  The PV waves' LDS reads are asm too, with
-// lgkmcnt waits counted by hand, so that the V reads of the next tile stay in
-// flight under the current tile's MFMAs.  A 4-slot ring of 36 KB tiles (32 keys):
-//   latent: key k at k*1024, 16-byte piece c at slot c ^ g(k),
-//           g(k) = ((k & 3) << 2) | ((k >> 1) & 3)
-//   rope:   key k at 32 KB + k*128, piece c at slot c ^ (k & 7)
-// keeps the QK ds_read_b128 pattern (8 lanes, 128 bytes per LDS cycle: the
-// low three bits of g are distinct over 8 consecutive keys) and the PV
-// ds_read_b64_tr_b16 pattern (32 lanes, 256 bytes per cycle: bits 2-3 of g
-// distinct over 4 consecutive keys) free of bank conflicts.
-//
+// Gather: LDS-DMA moves 16 bytes per lane straight into LDS.  PV wave c
+// gathers keys 8c .. 8c+7 of a tile with nine 64-lane global_load_lds_dwordx4,
+// one per 128-byte column group of the rows (8 latent groups, then the rope);
+// every lane keeps one 64-bit address (its key's row plus its piece, so rows
+// may lie past 4 GiB) and the instruction offset steps it from group to group
+// (the offset moves the LDS destination as well, so M0 advances by the rest
+// of a group).  The DMAs are asm: the compiler would otherwise make every LDS
+// read wait for them (it cannot tell the ring slots apart); the waits are
+// explicit vmcnt counts before each barrier.  The PV waves' LDS reads are asm
+// too, with lgkmcnt waits counted by hand, so that the V reads of the next
+// tile stay in flight under the current tile's MFMAs.  A 4-slot ring of 36 KB
+// tiles (32 keys), each four 9 KB units of 8 keys (the unit a wave gathers):
+//   unit u = key >> 3 at u*9216; group d (pieces 8d .. 8d+7 of the 8 keys) at
+//   +1024d; key k8 = key & 7 at +128 k8; piece p of the group at slot
+//   p ^ swz(k8), swz(k8) = ((k8 & 2) << 1) | ((k8 & 4) >> 1) | (k8 & 1).
+// The QK ds_read_b128 pattern (8 consecutive keys at one piece per LDS cycle)
+// hits 8 distinct slots because swz is a permutation; the PV
+// ds_read_b64_tr_b16 pattern (4 keys x 4 pieces x 2 halves per 32 lanes)
+// covers all 64 banks because swz(k8) ^ swz(k8 + 2) has bit 2 set for the
+// key pairs that share a bank half.  A lane's K fragment of step st is at a
+// fixed base ^ 64(st & 1) + 1024(st >> 1); its V^T fragment (4ks + cb) at a
+// fixed base ^ 64(cb & 1) + 18432 ks + 1024(cb >> 1).
+
 // Softmax reference: each row keeps a reference m (log2 units) instead of a
 // running max, so the accumulators are never rescaled.  The first tile sets m
 // to the row's max over that tile (the two QK waves of a row pair exchange
@@ -86,46 +92,22 @@ constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kSlack = 40.0f;
 constexpr int kKT = 32;                       // keys per tile
 constexpr int kTileLds = kKT * kDqk * 2;      // 36864 B
-constexpr int kRopeOff = kKT * 1024;          // rope parts after the 32 latent rows
+constexpr int kUnit = 8 * kDqk * 2;            // 9216 B: the 8 keys one wave gathers
+constexpr int kGroup = 1024;                  // 16-byte pieces 8d .. 8d+7 of the unit's 8 keys
+// LDS-DMA M0 step between the nine DMAs of a gather, which share one address
+// register and advance their source with the instruction offset (128 B per
+// group); the offset also moves the LDS destination, so M0 advances by the
+// rest of a group
+constexpr int kM0Step = kGroup - 128;
 constexpr int kRing = 4;                      // tiles staged in LDS
 constexpr int kQSteps = kDqk / 32;            // 18 steps of v_mfma_f32_16x16x32_bf16
 constexpr int kPreQK = 4;                     // K fragments read ahead
-constexpr int kRsrcWord3 = 0x00020000;
 constexpr int kCompactBatch = 64;             // requests scanned per workgroup to list real items
 
-__device__ __forceinline__ int swz_latent(int k) { return ((k & 3) << 2) | ((k >> 1) & 3); }
-__device__ __forceinline__ int swz_rope(int k) { return k & 7; }
+// slot of piece p (0..7) of key k8 (0..7) inside a group: p ^ swz(k8)
+__device__ __forceinline__ int swz(int k8) { return ((k8 & 2) << 1) | ((k8 & 4) >> 1) | (k8 & 1); }
 
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-
-__device__ __forceinline__ void dma16_global(const void* src, uint32_t lds_addr) {
-  uint32_t saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %2\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, off\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "v"(src), "s"(lds_addr)
-      : "memory");
-}
-
-// Buffer LDS-DMA of 16 bytes per lane (row descriptor, per-lane offset) into
-// LDS at lds_addr + 16*lane, issued as asm like dma16_global: the compiler
-// neither waits for it nor treats later LDS reads as possibly aliasing it.
-__device__ __forceinline__ void dma16_buffer(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, uint32_t lds_addr) {
-  uint32_t saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %3\n\t"
-      "s_nop 0\n\t"
-      "buffer_load_dwordx4 %1, %2, 0 offen lds\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "v"(voff), "s"(rsrc), "s"(lds_addr)
-      : "memory");
-}
 
 // A 4-byte global load issued as asm: its result is valid only after an
 // explicit vmcnt wait that names the register.
@@ -165,7 +147,7 @@ __device__ __forceinline__ bf16x8 ds_b128(uint32_t addr, int off) {
 __device__ __forceinline__ i16x4 ds_tr(uint32_t addr, int off) {
   i16x4 v;
   switch (off) {
-    VAMLA_TR_CASE(0) VAMLA_TR_CASE(16384)
+    VAMLA_TR_CASE(0) VAMLA_TR_CASE(1024) VAMLA_TR_CASE(18432) VAMLA_TR_CASE(19456)
     default: __builtin_trap();
   }
   return v;
@@ -198,21 +180,34 @@ __device__ __forceinline__ float sum4(float x) {
   return p + q;
 }
 
-// Gather instruction d (0..8) of PV wave c for one 32-key tile: d < 8 moves
-// the 1 KB latent part of key 8c+d (slot read out of lane 8d of sv), d = 8 the
-// 128-byte rope parts of keys 8c .. 8c+7 (lane l: key 8c + (l >> 3)).
-__device__ __forceinline__ void gather_one(const uint16_t* pool, uint32_t sv, uint8_t* buf, int c, int lane, int d) {
-  if (d < 8) {
-    const uint32_t slot = __builtin_amdgcn_readlane(sv, 8 * d);
-    const int key = 8 * c + d;
-    const __amdgpu_buffer_rsrc_t row = __builtin_amdgcn_make_buffer_rsrc((void*)(pool + (size_t)slot * kDqk), 0, 1024,
-                                                                         kRsrcWord3);
-    dma16_buffer(row, (uint32_t)((lane ^ swz_latent(key)) << 4), (uint32_t)(uintptr_t)(lds_void*)(buf + key * 1024));
-  } else {
-    const int kl = 8 * c + (lane >> 3);
-    const uint8_t* src = (const uint8_t*)(pool + (size_t)sv * kDqk + 512) + (((lane & 7) ^ swz_rope(kl)) << 4);
-    dma16_global(src, (uint32_t)(uintptr_t)(lds_void*)(buf + kRopeOff + 8 * c * 128));
-  }
+// The nine LDS-DMAs that gather PV wave c's 8 keys of a 32-key tile (keys
+// 8c .. 8c+7, unit c of the tile).  Lane l moves, for group d = 0..8, the
+// 16-byte piece 8d + ((l & 7) ^ swz(l >> 3)) of key 8c + (l >> 3) into LDS at
+// unit + 1024 d + 16 l, i.e. to slot l & 7 of that key's 128 bytes of the
+// group.  One 64-bit address per lane (its key's row plus its piece) serves
+// all nine: the instruction offset steps the source by 128 B per group.
+// sv: slot index of key 8c + (lane >> 3); pool_lane: pool + this lane's
+// piece offset.
+__device__ __forceinline__ void gather_tile(const uint8_t* pool_lane, uint32_t sv, uint8_t* buf, int c) {
+  const uint8_t* src = pool_lane + (size_t)sv * (kDqk * 2);
+  const uint32_t m = (uint32_t)(uintptr_t)(lds_void*)(buf + c * kUnit);
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %3\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off offset:128\n\t"
+      "s_mov_b32 m0, %4\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off offset:256\n\t"
+      "s_mov_b32 m0, %5\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off offset:384\n\t"
+      "s_mov_b32 m0, %6\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off offset:512\n\t"
+      "s_mov_b32 m0, %7\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off offset:640\n\t"
+      "s_mov_b32 m0, %8\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off offset:768\n\t"
+      "s_mov_b32 m0, %9\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off offset:896\n\t"
+      "s_mov_b32 m0, %10\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off offset:1024\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(src), "s"(m), "s"(m + 1 * kM0Step), "s"(m + 2 * kM0Step), "s"(m + 3 * kM0Step), "s"(m + 4 * kM0Step),
+        "s"(m + 5 * kM0Step), "s"(m + 6 * kM0Step), "s"(m + 7 * kM0Step), "s"(m + 8 * kM0Step)
+      : "memory");
 }
 
 struct Shared {
@@ -367,9 +362,10 @@ __global__ __launch_bounds__(512, 1) void prefix_splitkv_kernel(PrefixArgs a) {
         qf[st][nb] = ok ? v : bf16x8{};
       }
     }
-    const int key = 16 * hf + l16;
-    const int qk_lat = (key * 1024) | ((q4 ^ swz_latent(key)) << 4);
-    const int qk_rope = (kRopeOff + key * 128) | ((q4 ^ swz_rope(key)) << 4);
+    // K fragment of step st: key 16hf + l16 = unit 2hf + (l16 >> 3), key
+    // l16 & 7 of it; pieces 4st + q4 = group st >> 1, piece 4(st & 1) + q4
+    const int k8 = l16 & 7;
+    const int qk_base = (2 * hf + (l16 >> 3)) * kUnit + k8 * 128 + ((q4 ^ swz(k8)) << 4);
     float m_ref[2] = {-INFINITY, -INFINITY};   // rows 16nb + l16 of the pair
     float lsum[2] = {0.f, 0.f};
     bool have_ref = false;
@@ -399,16 +395,10 @@ __global__ __launch_bounds__(512, 1) void prefix_splitkv_kernel(PrefixArgs a) {
       for (int it = 0; it <= ntiles + 1; ++it) {
         typedef __attribute__((address_space(3))) const bf16x8 lds_frag;
         const uint32_t slot = lds_addr(ring(it));
-        const lds_frag* kp[4];
-        const lds_frag* kpr[2];
+        const lds_frag* kp[2];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) kp[j] = (const lds_frag*)(uintptr_t)(slot + (uint32_t)(qk_lat ^ (64 * j)));
-#pragma unroll
-        for (int j = 0; j < 2; ++j) kpr[j] = (const lds_frag*)(uintptr_t)(slot + (uint32_t)(qk_rope ^ (64 * j)));
-        auto kfrag = [&](int st) {
-          if (st < 16) return kp[st & 3][16 * (st >> 2)];
-          return kpr[st - 16][0];
-        };
+        for (int j = 0; j < 2; ++j) kp[j] = (const lds_frag*)(uintptr_t)(slot + (uint32_t)(qk_base ^ (64 * j)));
+        auto kfrag = [&](int st) { return kp[st & 1][(kGroup / 16) * (st >> 1)]; };
         // restart vote on tile it-2 (its softmax ran in the iteration before),
         // read ahead of the K fragments so that its wait does not cover them
         f32x4 vote = f32x4{};
@@ -548,15 +538,22 @@ __global__ __launch_bounds__(512, 1) void prefix_splitkv_kernel(PrefixArgs a) {
 #pragma unroll
   for (int d = 0; d < 8; ++d) o[d] = f32x16{};
   // transposed V reads: lane (block bb = lane/16, e = (lane/4)%4, s2 = lane%4)
+  // reads columns 128c + 32cb + 16(bb & 1) + 4s2 .. +3 of key
+  // 16ks + 8(bb >> 1) + e + 4hi: unit 2ks + (bb >> 1), key e + 4hi of it,
+  // piece 16c + 4cb + 2(bb & 1) + (s2 >> 1) = group 2c + (cb >> 1), piece
+  // 4(cb & 1) + 2(bb & 1) + (s2 >> 1) of the group, half s2 & 1 of the piece
   int pvb[2];
   {
     const int bb = lane >> 4, e = (lane >> 2) & 3, s2 = lane & 3;
 #pragma unroll
     for (int hi = 0; hi < 2; ++hi) {
-      const int key = 8 * (bb >> 1) + e + 4 * hi;
-      pvb[hi] = (key * 1024 + 256 * c + 8 * (s2 & 1)) | (((2 * (bb & 1) + (s2 >> 1)) ^ swz_latent(key)) << 4);
+      const int kk = e + 4 * hi;
+      pvb[hi] = (bb >> 1) * kUnit + 2 * c * kGroup + kk * 128 + (((2 * (bb & 1) + (s2 >> 1)) ^ swz(kk)) << 4) +
+                8 * (s2 & 1);
     }
   }
+  // this lane's piece offset inside a row (see gather_tile)
+  const uint8_t* pool_lane = (const uint8_t*)a.pool + (((lane & 7) ^ swz(lane >> 3)) << 4);
   // slots of tile t; valid after the next vmcnt wait
   auto load_slot = [&](int t) -> uint32_t { return load_u32_async(slot_ptr(t, c)); };
   for (;;) {
@@ -569,11 +566,9 @@ __global__ __launch_bounds__(512, 1) void prefix_splitkv_kernel(PrefixArgs a) {
       const uint32_t s0 = slot_first[0], s1 = slot_first[1];
       svd = slot_first[2];
       svn = slot_first[3];
-#pragma unroll
-      for (int d = 0; d < 9; ++d) gather_one(a.pool, s0, tile0, c, lane, d);
+      gather_tile(pool_lane, s0, tile0, c);
       if (ntiles > 1) {
-#pragma unroll
-        for (int d = 0; d < 9; ++d) gather_one(a.pool, s1, tile1, c, lane, d);
+        gather_tile(pool_lane, s1, tile1, c);
       }
     }
     // tile 0 must have landed; tile 1's nine gathers may stay in flight
@@ -581,17 +576,18 @@ __global__ __launch_bounds__(512, 1) void prefix_splitkv_kernel(PrefixArgs a) {
     if (ntiles > 1) asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
     else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    // V^T fragment f = 4ks + cb of a tile: two transposed reads at
-    // slot + vad[cb][hi] + 16384 ks
-    uint32_t vad[4][2];
+    // V^T fragment f = 4ks + cb: two transposed reads at
+    // slot + vad[cb & 1][hi] + (2 units) ks + (1 group) (cb >> 1)
+    uint32_t vad[2][2];
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb)
+    for (int cp = 0; cp < 2; ++cp)
 #pragma unroll
-      for (int hi = 0; hi < 2; ++hi) vad[cb][hi] = (uint32_t)(pvb[hi] ^ (64 * cb));
+      for (int hi = 0; hi < 2; ++hi) vad[cp][hi] = (uint32_t)(pvb[hi] ^ (64 * cp));
     auto vread = [&](uint32_t slot, int f) {
       const int ks = f >> 2, cb = f & 3;
-      const i16x4 lo = ds_tr(slot + vad[cb][0], ks * 16384);
-      const i16x4 hi = ds_tr(slot + vad[cb][1], ks * 16384);
+      const int off = ks * 2 * kUnit + (cb >> 1) * kGroup;
+      const i16x4 lo = ds_tr(slot + vad[cb & 1][0], off);
+      const i16x4 hi = ds_tr(slot + vad[cb & 1][1], off);
       return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
     };
     const uint32_t pb_addr[2] = {lds_addr(sh.pbuf[0][0]) + 16 * lane, lds_addr(sh.pbuf[1][0]) + 16 * lane};
@@ -629,8 +625,7 @@ __global__ __launch_bounds__(512, 1) void prefix_splitkv_kernel(PrefixArgs a) {
           // matrix core idle at the top of the iteration; issued later, the
           // rows arrive late
           if (f == 1 && do_dma) {
-#pragma unroll
-            for (int d = 0; d < 9; ++d) gather_one(a.pool, svd, dbuf, c, lane, d);
+            gather_tile(pool_lane, svd, dbuf, c);
             __builtin_amdgcn_sched_barrier(0);
           }
         }
@@ -640,8 +635,7 @@ __global__ __launch_bounds__(512, 1) void prefix_splitkv_kernel(PrefixArgs a) {
           for (int f = 0; f < 8; ++f) vf[f] = vread(nslot, f);
         }
         if (do_dma) {
-#pragma unroll
-          for (int d = 0; d < 9; ++d) gather_one(a.pool, svd, dbuf, c, lane, d);
+          gather_tile(pool_lane, svd, dbuf, c);
         }
       }
       // the gather of tile it+1 (issued one iteration ago) and the slot load
