@@ -51,7 +51,7 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
 # their sha256, and reported as null for any other build.
 MEASURED_TRAFFIC = {
     # sha256(prefix_splitkv.hip + kernels.h): (fetch KiB, write KiB, fetch scale, write scale)
-    "190e069271bcba886b49308bcb5ce3358ca784d9155afbbf36a886ff0507236f": (59208.1, 31260.9, 2.0, 1.0),
+    "fc54252da781eef9745bdf49028dc9036ea89103cd1d25200c91df10b4a97632": (59434.9, 31260.9, 2.0, 1.0),
 }
 KERNEL_SOURCES = ("prefix_splitkv.hip", "kernels.h")
 KV_ROW_BYTES = 576 * 2
@@ -215,7 +215,7 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--config", type=int, default=3)
-    ap.add_argument("--slot-mode", default=None, choices=["scrambled", "contiguous", "churned"],
+    ap.add_argument("--slot-mode", default=None, choices=["scrambled", "contiguous", "churned", "churned_sorted"],
                     help="slot layout of the pool (default: the workload's own)")
     ap.add_argument("--launch", default="eager", choices=["eager", "graph"],
                     help="eager: one library call per step; graph: each step replays a captured HIP graph "
@@ -230,6 +230,9 @@ def main():
                     help="standard deviation of the query values (0.1: score sd ~0.017 nats; 17.3: ~3 nats, a "
                          "realistic logit spread)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--warm-seconds", type=float, default=WARM_SECONDS,
+                    help="after the --warmup steps, keep stepping until this much wall time has passed "
+                         "(0 for counter runs under a profiler)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 512 MiB device copy (counter calibration under rocprofv3 --pmc)")
     args = ap.parse_args()
@@ -341,13 +344,13 @@ def main():
         step(i)
         n_warm += 1
     torch.cuda.synchronize()
-    while time.perf_counter() - t_warm < WARM_SECONDS:
+    while time.perf_counter() - t_warm < args.warm_seconds:
         for _ in range(8):
             step(n_warm)
             n_warm += 1
         torch.cuda.synchronize()
     warm_s = time.perf_counter() - t_warm
-    err(f"[bench] warmup: {n_warm} steps in {warm_s:.2f} s (at least {args.warmup} steps and {WARM_SECONDS} s)")
+    err(f"[bench] warmup: {n_warm} steps in {warm_s:.2f} s (at least {args.warmup} steps and {args.warm_seconds} s)")
 
     # --- timed region: exactly K steps ---
     torch.cuda.synchronize()

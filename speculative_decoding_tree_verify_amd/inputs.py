@@ -123,38 +123,56 @@ def all_parent_arrays(n: int):
 class FreeListAllocator:
     """page_size=1 free list: alloc(n) takes the first n free slots, free()
     appends slots to the end.  Slot 0 is never handed out.  Backed by a ring
-    buffer so 2M-slot pools stay cheap."""
+    buffer so 2M-slot pools stay cheap.
 
-    def __init__(self, pool_slots: int):
+    sorted=True keeps the free list in slot order instead: alloc(n) takes the
+    n lowest free slots (a bitmap of free slots), so freed holes are refilled
+    first and long runs stay free at the top of the pool."""
+
+    def __init__(self, pool_slots: int, sorted: bool = False):
         self.cap = pool_slots
-        self.ring = np.zeros(pool_slots, dtype=np.int64)
-        self.ring[: pool_slots - 1] = np.arange(1, pool_slots, dtype=np.int64)
-        self.head = 0
+        self.sorted = sorted
         self.size = pool_slots - 1
+        if sorted:
+            self.free_mask = np.ones(pool_slots, dtype=bool)
+            self.free_mask[0] = False
+        else:
+            self.ring = np.zeros(pool_slots, dtype=np.int64)
+            self.ring[: pool_slots - 1] = np.arange(1, pool_slots, dtype=np.int64)
+            self.head = 0
 
     def alloc(self, n: int) -> np.ndarray:
         if n > self.size:
             raise MemoryError("pool exhausted")
-        idx = (self.head + np.arange(n)) % self.cap
-        out = self.ring[idx].copy()
-        self.head = (self.head + n) % self.cap
+        if self.sorted:
+            out = np.flatnonzero(self.free_mask)[:n].astype(np.int64)
+            self.free_mask[out] = False
+        else:
+            idx = (self.head + np.arange(n)) % self.cap
+            out = self.ring[idx].copy()
+            self.head = (self.head + n) % self.cap
         self.size -= n
         return out
 
     def free(self, slots: np.ndarray) -> None:
         n = len(slots)
-        tail = (self.head + self.size) % self.cap
-        idx = (tail + np.arange(n)) % self.cap
-        self.ring[idx] = slots
+        if self.sorted:
+            self.free_mask[slots] = True
+        else:
+            tail = (self.head + self.size) % self.cap
+            idx = (tail + np.arange(n)) % self.cap
+            self.ring[idx] = slots
         self.size += n
 
 
 def churned_allocator(pool_slots: int, reserve: int, rng: np.random.Generator,
-                      n_requests: int = 10_000, lo: int = 64, hi: int = 16384) -> FreeListAllocator:
+                      n_requests: int = 10_000, lo: int = 64, hi: int = 16384,
+                      sorted: bool = False) -> FreeListAllocator:
     """Replay `n_requests` allocations with sizes ~ logU[lo, hi]; before each
     alloc, free random live requests until the free list holds size + reserve;
-    after each alloc, free one random live request with probability 1/2."""
-    a = FreeListAllocator(pool_slots)
+    after each alloc, free one random live request with probability 1/2.
+    sorted selects the sorted free list (lowest free slots first)."""
+    a = FreeListAllocator(pool_slots, sorted=sorted)
     live: List[np.ndarray] = []
     llo, lhi = math.log(lo), math.log(hi)
     for _ in range(n_requests):
@@ -210,7 +228,9 @@ def make_inputs(prefix_lens: Sequence[int], parents: Sequence[np.ndarray], num_h
                 pool_slots: int, slot_mode: str, seed: int, std_q: float = 0.1,
                 std_kv: float = 0.1, poison_unused: bool = True,
                 churn_requests: int = 10_000) -> VerifyInputs:
-    """Build one batch.  slot_mode in {"contiguous", "scrambled", "churned"}.
+    """Build one batch.  slot_mode in {"contiguous", "scrambled", "churned",
+    "churned_sorted"} (the last two replay the free-list or the sorted-free-list
+    allocator).
 
     Streams spawned from SeedSequence(seed): [tree-independent] slots, pool, q.
     Logical rows (prefix then tree, per request) get their values in logical
@@ -230,8 +250,9 @@ def make_inputs(prefix_lens: Sequence[int], parents: Sequence[np.ndarray], num_h
         logical_slots = np.arange(1, need + 1, dtype=np.int64)
     elif slot_mode == "scrambled":
         logical_slots = s_slots.permutation(np.arange(1, pool_slots, dtype=np.int64))[:need]
-    elif slot_mode == "churned":
-        alloc = churned_allocator(pool_slots, need, s_slots, n_requests=churn_requests)
+    elif slot_mode in ("churned", "churned_sorted"):
+        alloc = churned_allocator(pool_slots, need, s_slots, n_requests=churn_requests,
+                                  sorted=slot_mode == "churned_sorted")
         parts = []
         for b in range(B):
             parts.append(alloc.alloc(Ls[b]))

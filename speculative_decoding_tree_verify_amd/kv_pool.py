@@ -151,29 +151,43 @@ def accepted_path(parent: Sequence[int], leaf: int) -> List[int]:
 
 
 class Tier0Defrag:
-    """The Tier-0 policy: keep long-lived requests in contiguous runs.
+    """The Tier-0 policy: keep long-lived requests in contiguous runs when
+    that pays.
 
     compact(req) moves a request's prefix rows into one contiguous run, with
     `headroom` free slots after it reserved for the tokens the request will
     accept, when its rows are split over more than one run and such a run is
-    free.  should_compact() prices that one-time copy against the per-step
-    gain of a contiguous layout: compact when the request's expected
-    remaining steps reach `payback_steps` (the copy time over the per-step
-    saving, as bench.py --compaction-payback measures it).
+    free.  should_compact(req, expected_steps) prices that one-time copy
+    against the per-step gain of a contiguous layout: compact when
+    expected_steps * step_gain_us >= rows * gather_us_per_row.  Both figures
+    are measurements (bench.py --defrag: the step on scattered and on
+    contiguous slots, and the gather's rate); with this library's verify
+    kernel the per-step gain measured on the 8k-prefix and 128k-prefix decode
+    workloads is nil (the kernel reads each 1152-byte row whole, wherever it
+    sits), so the default step_gain_us = 0 never compacts.
 
     commit_accepted(req, ...) appends the accepted path of a verified tree to
     the request: its rows move from their scattered tree slots into the
     request's reserve (or the free slots right after its run, or else a new
-    run of their own), and every tree slot of the step is freed.
+    run of their own), and every tree slot of the step is freed.  That move is
+    at most 65 rows, so it is done whatever the policy.
     """
 
-    def __init__(self, allocator: SlotAllocator, payback_steps: float = 40.0, headroom: int = 64):
+    def __init__(self, allocator: SlotAllocator, step_gain_us: float = 0.0, gather_us_per_row: float = 0.39e-3,
+                 headroom: int = 64):
         self.alloc = allocator
-        self.payback_steps = float(payback_steps)
+        self.step_gain_us = float(step_gain_us)
+        self.gather_us_per_row = float(gather_us_per_row)
         self.headroom = int(headroom)
 
+    def payback_steps(self, req: Request) -> float:
+        """Steps after which compacting req pays back (inf when never)."""
+        if self.step_gain_us <= 0:
+            return float("inf")
+        return req.length * self.gather_us_per_row / self.step_gain_us
+
     def should_compact(self, req: Request, expected_steps: float) -> bool:
-        return count_runs(req.prefix) > 1 and expected_steps >= self.payback_steps
+        return count_runs(req.prefix) > 1 and expected_steps >= self.payback_steps(req)
 
     def release(self, req: Request) -> None:
         """Free the request's rows and reserve (request finished)."""

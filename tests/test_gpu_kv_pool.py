@@ -59,7 +59,7 @@ def test_compaction_and_commit_keep_results_and_rows():
     out0, lse0 = _verify(pool_t, q, req.prefix, tree, parent)
 
     # Tier-0 compaction: one run, vacated slots poisoned, bit-identical result
-    pol = kp.Tier0Defrag(alloc, payback_steps=40, headroom=32)
+    pol = kp.Tier0Defrag(alloc, step_gain_us=1.0, headroom=32)
     old_prefix = req.prefix.copy()
     assert pol.should_compact(req, expected_steps=1000)
     assert pol.compact(req, pool_t)

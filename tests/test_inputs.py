@@ -74,3 +74,28 @@ def test_config_1_shapes():
     x = gen.config_inputs(1)
     assert x.q.shape == (9, 16, 576) and x.pool.shape == (4096, 576)
     assert x.total_prefix == 1024 and x.total_tree == 9
+
+
+def test_sorted_allocator_takes_the_lowest_free_slots():
+    a = gen.FreeListAllocator(12, sorted=True)
+    x = a.alloc(6)                       # 1..6
+    assert list(x) == [1, 2, 3, 4, 5, 6]
+    a.free(np.array([5, 2]))
+    assert list(a.alloc(3)) == [2, 5, 7]
+    assert a.size == 12 - 1 - 7
+
+
+def test_sorted_churn_leaves_fewer_runs_than_the_free_list():
+    # the same churn replayed with both policies: the sorted list refills holes
+    # first, so a request allocated afterwards spans fewer runs
+    def runs(s):
+        return int(1 + np.count_nonzero(np.diff(s) != 1))
+    out = {}
+    for srt in (False, True):
+        a = gen.churned_allocator(1 << 15, 3000, np.random.default_rng(9), n_requests=300, lo=16, hi=2048, sorted=srt)
+        out[srt] = runs(a.alloc(3000))
+    assert out[True] <= out[False]
+    x = gen.make_inputs([2000], [gen.random_tree(9, np.random.default_rng(1))], 2, 1 << 14, "churned_sorted", seed=4,
+                        churn_requests=200)
+    used = np.concatenate([x.prefix_slot_idx, x.tree_slot_idx])
+    assert len(np.unique(used)) == used.size and used.min() >= 1

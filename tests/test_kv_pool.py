@@ -104,10 +104,13 @@ def _scattered_request(pool_slots=4096, L=700, N=9, seed=3):
 def test_compaction_moves_rows_into_one_run(host_gather):
     a, req, tree, pool = _scattered_request()
     rows = pool[req.prefix].copy()
-    pol = kp.Tier0Defrag(a, payback_steps=40, headroom=16)
+    # 700 rows at 1 us per 100 rows cost 7 us; a 0.1 us gain per step pays after 70 steps
+    pol = kp.Tier0Defrag(a, step_gain_us=0.1, gather_us_per_row=0.01, headroom=16)
     assert kp.count_runs(req.prefix) > 1
-    assert not pol.should_compact(req, expected_steps=10)
-    assert pol.should_compact(req, expected_steps=100)
+    assert abs(pol.payback_steps(req) - 70.0) < 1e-9
+    assert not pol.should_compact(req, expected_steps=69)
+    assert pol.should_compact(req, expected_steps=70)
+    assert not kp.Tier0Defrag(a).should_compact(req, expected_steps=1e12)   # no measured gain: never
     free_before = a.n_free
     assert pol.compact(req, pool)
     assert kp.count_runs(req.prefix) == 1
