@@ -142,9 +142,9 @@ typedef struct vamla_params {
  * restarts}, status being VAMLA_ERR_INVALID_LENGTHS / _TREE / _SLOT and
  * array 0 (cu_*), 1 (parent), 2 (prefix_slot_idx) or 3 (tree_slot_idx); the
  * first three are zero when the data is valid.  restarts counts the chunk
- * restarts of the split pass (a score more than 2^40 above a chunk's softmax
- * reference makes a work item start over with a higher one; see the split
- * kernel).  When the record is set, the split kernel does no work (no
+ * restarts of the split pass (a score more than 2^96, 66.5 nats, above the
+ * max of a work item's first key tile makes the item start over with a
+ * higher softmax reference; see the split kernel).  When the record is set, the split kernel does no work (no
  * index is dereferenced) and the merge writes NaN to every element of out and
  * lse (total_tree x H rows).  The call itself still returns VAMLA_OK: the
  * check runs asynchronously and the caller reads the record when it syncs.

@@ -63,17 +63,21 @@
 
 // Softmax reference: each row keeps a reference m (log2 units) instead of a
 // running max, so the accumulators are never rescaled.  The first tile sets m
-// to the row's max over that tile (the two QK waves of a row pair exchange
-// their halves through LDS at the first barrier).  While every score stays within kSlack of
-// m, exp2(s - m) <= 2^kSlack, inside bf16/fp32 range (the accumulators overflow
-// only if |V| * keys of a chunk reached 2^(128 - kSlack)).  A tile that breaks
-// this (a jump of more than 27 nats: rare) makes the workgroup restart its
-// item with each row's m raised to max(m, the row's max over that tile): rows
-// that did not break keep a reference at or below their true max, so no row's
-// exponentials drift towards underflow however many restarts there are; each
-// restart needs a new tile max more than kSlack above a reference, so there
-// are at most as many restarts as tiles.  With the debug flag the kernel adds
-// its restarts to a counter in the debug record.
+// to the row's max over that tile plus kMargin (the two QK waves of a row pair
+// exchange their halves through LDS at the first barrier).  While every score
+// stays within kSlack of m, exp2(s - m) <= 2^kSlack, inside bf16/fp32 range
+// (the accumulators overflow only if |V| * keys of a chunk reached
+// 2^(128 - kSlack)); the row's own max term is at least 2^-kMargin, so its sum
+// stays far from underflow, and only terms below 2^-126, under 2^-(126 -
+// kMargin) of the max term, can flush.  A tile that breaks this (a score more than kMargin + kSlack
+// = 96 log2 units, 66.5 nats, above the first tile's max: rare) makes the
+// workgroup restart its item with each row's m raised to max(m, the row's max
+// over that tile + kMargin).  Every m stays at or below the row's true max +
+// kMargin, so no row's exponentials drift towards underflow however many
+// restarts there are; each restart needs a new tile max more than kSlack above
+// a reference and leaves every row's m above that tile's max, so there are at
+// most as many restarts as tiles.  With the debug flag the kernel adds its
+// restarts to a counter in the debug record.
 
 #include "kernels.h"
 
@@ -89,7 +93,8 @@ typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 constexpr float kLn2 = 0.69314718055994530942f;
-constexpr float kSlack = 40.0f;
+constexpr float kSlack = 56.0f;               // headroom above the reference (log2)
+constexpr float kMargin = 40.0f;              // reference above the first tile's max (log2)
 constexpr int kKT = 32;                       // keys per tile
 constexpr int kTileLds = kKT * kDqk * 2;      // 36864 B
 constexpr int kUnit = 8 * kDqk * 2;            // 9216 B: the 8 keys one wave gathers
@@ -414,7 +419,7 @@ __global__ __launch_bounds__(512, 1) void prefix_splitkv_kernel(PrefixArgs a) {
           const int t = it - 1;
           if (t == 0 && !have_ref) {
 #pragma unroll
-            for (int nb = 0; nb < 2; ++nb) m_ref[nb] = pair_row_max(0, nb);
+            for (int nb = 0; nb < 2; ++nb) m_ref[nb] = pair_row_max(0, nb) + kMargin;
           }
           // P in bf16, stored in the PV B-operand layout: block (ks = hf,
           // rb = pr), lane L = j + 32*(q4 >> 1) holds keys 8*(q4 >> 1) .. +7 of
@@ -501,11 +506,12 @@ __global__ __launch_bounds__(512, 1) void prefix_splitkv_kernel(PrefixArgs a) {
       }
       if (!restart) break;
       ++restarts;
-      // restart with each row's reference raised to its max over the offending tile
+      // restart with each row's reference raised to its max over the
+      // offending tile + kMargin
       const int bad = restart_tile % 3;
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) {
-        m_ref[nb] = fmaxf(m_ref[nb], pair_row_max(bad, nb));
+        m_ref[nb] = fmaxf(m_ref[nb], pair_row_max(bad, nb) + kMargin);
         lsum[nb] = 0.f;
       }
       have_ref = true;

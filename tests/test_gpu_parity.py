@@ -131,6 +131,23 @@ def test_sharp_scores_move_the_reference():
     check(x, chunk=1024, what="sharp scores")
 
 
+def test_wide_score_spread_keeps_the_first_reference():
+    # query sd 80: score sd ~ 14 nats, so within a 1024-key chunk some rows
+    # climb 30-45 nats above their first tile's max.  The split kernel's
+    # reference sits a fixed margin above that max with headroom on top
+    # (66.5 nats in all), so no chunk restarts and every row matches
+    rng = np.random.default_rng(8)
+    x = small([3000], [gen.random_tree(9, rng)], 4, seed=20, std_q=80.0)
+    qm = vo.bf16_bits_to_f64(x.q).reshape(-1, 576)
+    km = vo.bf16_bits_to_f64(x.pool[x.prefix_slot_idx])
+    s = qm @ km.T * x.scale
+    jump = max((s[:, c:c + 1024].max(1) - s[:, c:c + 32].max(1)).max() for c in range(0, 3000, 1024))
+    log(f"[case] largest climb over a chunk's first tile: {jump:.1f} nats")
+    assert 30.0 < jump < 60.0
+    _, _, restarts = check_debug(x, 1024, "score sd 14 nats")
+    assert restarts == 0
+
+
 @pytest.mark.parametrize("H,N,node,head", [(2, 5, 2, 1), (5, 9, 8, 4)])
 @pytest.mark.parametrize("chunk", [2048, 32])
 def test_reference_jump_mid_chunk(chunk, H, N, node, head):
@@ -145,9 +162,10 @@ def test_reference_jump_mid_chunk(chunk, H, N, node, head):
     key = 1500
     slot = x.prefix_slot_idx[key]
     k = vo.bf16_bits_to_f64(x.pool[slot])
-    # score ~ 100*|k|^2*sigma ~ 42 nats above the rest: past the split kernel's
-    # 2^40 headroom, so with 2048-key chunks the chunk restarts
-    x.q[node, head] = gen.f32_to_bf16_bits((k * 100.0).astype(np.float32))
+    # score ~ 250*|k|^2*scale ~ 105 nats above the rest: past the split
+    # kernel's 66.5 nats of tolerance above a chunk's first key tile, so with
+    # 2048-key chunks the chunk restarts
+    x.q[node, head] = gen.f32_to_bf16_bits((k * 250.0).astype(np.float32))
     out, lse, restarts = check_debug(x, chunk, f"reference jump chunk={chunk} rows={H * N} node={node} head={head}")
     np.testing.assert_allclose(out[node, head], k[:512], atol=2e-2)
     if chunk == 2048:
@@ -176,15 +194,17 @@ def check_debug(x, chunk, what):
 
 
 def test_repeated_restarts_leave_other_rows_exact():
-    # one row meets four keys whose scores climb by ~42 nats each inside one
-    # 2048-key chunk: four restarts of the chunk.  Every other row of the tile
-    # (same row pair included) keeps a reference at or below its own max, so
-    # all rows still match the oracle, and the climbing row ends on the last key
+    # one row meets keys whose scores climb by ~105 nats at a time inside one
+    # 2048-key chunk (key 100 and its copy at 300, then 2x, 3x, 4x it): four
+    # restarts of the chunk.  Every other row of the tile
+    # (same row pair included) keeps a reference at or below its own max plus
+    # the fixed margin, so all rows still match the oracle, and the climbing
+    # row ends on the last key
     rng = np.random.default_rng(70)
     H, N, node, head = 4, 9, 3, 2
     x = small([2000], [gen.random_tree(N, rng)], H, seed=71)
     k = vo.bf16_bits_to_f64(x.pool[x.prefix_slot_idx[100]])
-    x.q[node, head] = gen.f32_to_bf16_bits((k * 100.0).astype(np.float32))
+    x.q[node, head] = gen.f32_to_bf16_bits((k * 250.0).astype(np.float32))
     for g, pos in enumerate((300, 700, 1100, 1500), start=1):
         x.pool[x.prefix_slot_idx[pos]] = gen.f32_to_bf16_bits((k * g).astype(np.float32))
     out, lse, restarts = check_debug(x, 2048, "four climbing keys in one chunk")
