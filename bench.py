@@ -51,7 +51,7 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
 # their sha256, and reported as null for any other build.
 MEASURED_TRAFFIC = {
     # sha256(prefix_splitkv.hip + kernels.h): (fetch KiB, write KiB, fetch scale, write scale)
-    "fc54252da781eef9745bdf49028dc9036ea89103cd1d25200c91df10b4a97632": (59434.9, 31260.9, 2.0, 1.0),
+    "895e90703575b71dc248e557d62dc2f447742b429e59cac5e2458298b0df3a0f": (59335.0, 31260.9, 2.0, 1.0),
 }
 KERNEL_SOURCES = ("prefix_splitkv.hip", "kernels.h")
 KV_ROW_BYTES = 576 * 2
@@ -363,8 +363,8 @@ def main():
     value = alg["kv_bytes"] / (ms_per_step * 1e-3) / 1e9
 
     # chunk restarts of the split pass on this workload (one call with the
-    # debug flag, outside the timed region): a score more than 2^40 above a
-    # chunk's softmax reference makes a work item start over
+    # debug flag, outside the timed region): a score climbing more than
+    # 66.5 nats above a work item's first key tile makes the item start over
     prob_dbg = vb.Problem(**{**prob.__dict__, "flags": prob.flags | vb.FLAG_DEBUG_VALIDATE})
     vb.split_partials(prob_dbg, q, pools[0], pre, tre, par, cup, cut, ws)
     torch.cuda.synchronize()
@@ -403,13 +403,26 @@ def main():
     err(f"[bench] split kernel timing passes (us): {[round(v * 1e3, 1) for v in split_passes]}")
     ms_merge = time_after(split_only, merge_only, iters)
     ms_step_ev = time_events(step, iters)
-    pct = warm = copy_gbs = None
+    pct = warm = copy_gbs = read_ceiling = None
     if not args.calib_copy:   # counter runs keep to the copies they calibrate against
         pct = step_percentiles(step, iters)
         warm = step_percentiles(lambda i: step(0), iters)
         copy_gbs = copy_rate_gbs()
         err(f"[bench] per-step us p10/p50/p90: {pct} (pool copies rotated), {warm} (one pool copy, warm); "
             f"device copy {copy_gbs:.0f} GB/s")
+        # the same rows read and nothing else (vamla_read_rows): the rate a
+        # scattered read of this step's KV rows reaches on this chip
+        rows_all = torch.cat([pre[:x.total_prefix], tre])
+        sink = torch.empty(vb.READ_ROWS_SINK_WORDS, dtype=torch.int32, device=dev)
+        vb.read_rows(pools[0], rows_all, sink)   # first launch of the kernel loads its code object
+        ms_read = time_events(lambda i: vb.read_rows(pools[i % n_copies], rows_all, sink), iters)
+        read_ceiling = {"us": round(ms_read * 1e3, 2),
+                        "gbs": round(alg["kv_bytes"] / (ms_read * 1e-3) / 1e9, 1),
+                        "split_us_over_read_us": round(ms_read / ms_split, 4),
+                        "step_us_over_read_us": round(ms_read / ms_step_ev, 4)}
+        err(f"[bench] plain read of the step's {rows_all.numel()} KV rows: {ms_read * 1e3:.1f} us "
+            f"({read_ceiling['gbs']:.0f} GB/s); split pass at {read_ceiling['split_us_over_read_us'] * 100:.1f}% "
+            f"of that rate, whole step at {read_ceiling['step_us_over_read_us'] * 100:.1f}%")
     # algorithmic flops of the split kernel: every (row, visible key) pair, prefix and tree
     flops = alg["prefix_flops"] + alg["tail_flops"]
     achieved = flops / (ms_split * 1e-3) / 1e12
@@ -468,6 +481,7 @@ def main():
             "step_us_p10_p50_p90": pct,
             "step_us_warm_p10_p50_p90": warm,
             "device_copy_gbs": round(copy_gbs, 1) if copy_gbs else None,
+            "kv_read_ceiling": read_ceiling,
             "pct_of_device_copy": round(value / copy_gbs * 100, 3) if copy_gbs else None,
             "defrag_us": defrag_us,
         },

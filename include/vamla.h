@@ -291,6 +291,23 @@ int verify_attn_mla_static(const vamla_params* p, const uint16_t* q, const uint1
 int vamla_slot_gather(const uint16_t* kv_pool, const int32_t* idx, int64_t n, uint16_t* dst,
                       void* stream);
 
+/*
+ * Read-rate calibration: reads the n pool rows kv_pool[idx[l], :] (1152 bytes
+ * each) and does nothing with them but fold them into a checksum.  It times
+ * what a plain read of exactly the rows a verify step gathers costs, the
+ * practical ceiling of the split pass where it is HBM-bound (the pages
+ * measure verify kernels by effective KV-read bandwidth against the HBM peak:
+ * "The Anatomy of a Kernel Investigation", "Phase 3").
+ *   kv_pool device bf16 [*, 576]; idx device int32 [n] (slots must be valid);
+ *   sink device uint32 [VAMLA_READ_ROWS_SINK_WORDS], fully overwritten: the
+ *   XOR of its words equals the XOR of every 32-bit word of the n rows (all
+ *   zero for n = 0).
+ * Returns VAMLA_ERR_INVALID_ARG for n < 0 or a null pointer (idx may be null
+ * when n = 0).  Enqueued on stream; no allocation, no sync.
+ */
+#define VAMLA_READ_ROWS_SINK_WORDS 4608
+int vamla_read_rows(const uint16_t* kv_pool, const int32_t* idx, int64_t n, uint32_t* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

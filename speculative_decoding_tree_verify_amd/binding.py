@@ -32,9 +32,11 @@ STATUS = {
     -8: "VAMLA_ERR_INVALID_LENGTHS", -9: "VAMLA_ERR_STATIC_LIMIT",
 }
 STATIC_WORKSPACE_BYTES = 64 << 20
+READ_ROWS_SINK_WORDS = 4608                # include/vamla.h VAMLA_READ_ROWS_SINK_WORDS
 
 EXPORTS = ("vamla_status_string", "vamla_plan", "vamla_workspace_size", "vamla_validate", "verify_attn_mla",
-           "vamla_split_partials", "vamla_lse_merge", "vamla_slot_gather", "verify_attn_mla_static")
+           "vamla_split_partials", "vamla_lse_merge", "vamla_slot_gather", "verify_attn_mla_static",
+           "vamla_read_rows")
 
 
 class VamlaParams(ctypes.Structure):
@@ -100,6 +102,7 @@ def lib() -> ctypes.CDLL:
     L.vamla_lse_merge.argtypes = [P(VamlaParams), vp, vp, vp]
     L.vamla_slot_gather.argtypes = [vp, vp, i64, vp, vp]
     L.verify_attn_mla_static.argtypes = [P(VamlaParams), vp, vp, vp, vp, vp, vp, vp, vp]
+    L.vamla_read_rows.argtypes = [vp, vp, i64, vp, vp]
     for name in EXPORTS:
         if name != "vamla_status_string":
             getattr(L, name).restype = ctypes.c_int
@@ -368,6 +371,23 @@ def slot_gather(kv_pool, idx, dst=None, stream=None):
     _check(lib().vamla_slot_gather(_ptr(_bits(kv_pool, "kv_pool")), _ptr(idx) if n else None, n,
                                    _ptr(dst) if n else None, _stream(stream)), "vamla_slot_gather")
     return dst
+
+
+def read_rows(kv_pool, idx, sink=None, stream=None):
+    """Reads the rows kv_pool[idx] and folds them into sink (uint32
+    [READ_ROWS_SINK_WORDS], as int32): the XOR of its words is the XOR of every
+    32-bit word of those rows.  A read-rate calibration, no compute."""
+    torch = _torch()
+    _index(idx, 0, "idx")
+    if kv_pool.dim() != 2 or kv_pool.shape[1] != D_QK or kv_pool.dtype not in _bf16_like():
+        raise ValueError(f"kv_pool must be bfloat16 [P, {D_QK}], got {kv_pool.dtype} {tuple(kv_pool.shape)}")
+    if sink is None:
+        sink = torch.empty(READ_ROWS_SINK_WORDS, dtype=torch.int32, device=kv_pool.device)
+    _shaped(sink, (READ_ROWS_SINK_WORDS,), (torch.int32,), "sink")
+    n = idx.numel()
+    _check(lib().vamla_read_rows(_ptr(_bits(kv_pool, "kv_pool")), _ptr(idx) if n else None, n, _ptr(sink),
+                                 _stream(stream)), "vamla_read_rows")
+    return sink
 
 
 def workspace_views(prob: Problem, ws: Workspace):

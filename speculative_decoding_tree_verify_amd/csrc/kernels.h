@@ -98,6 +98,12 @@ __device__ __forceinline__ int device_chunk(const int32_t* cu_prefix, int batch,
 hipError_t launch_prefix_splitkv(const PrefixArgs& a, hipStream_t stream);
 hipError_t launch_lse_merge(const MergeArgs& a, hipStream_t stream);
 hipError_t launch_debug_validate(const ValidateArgs& a, hipStream_t stream);
+// Read of n pool rows by slot index, folded into VAMLA_READ_ROWS_SINK_WORDS
+// XOR words (a fixed grid of kReadRowsBlocks blocks, two per CU).
+constexpr int kReadRowsBlocks = 512;
+hipError_t launch_read_rows(const uint16_t* pool, const int32_t* idx, int64_t n, uint32_t* sink,
+                            hipStream_t stream);
+
 hipError_t launch_slot_gather(const uint16_t* pool, const int32_t* idx, int64_t n, uint16_t* dst,
                               hipStream_t stream);
 

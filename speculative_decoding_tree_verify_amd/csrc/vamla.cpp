@@ -360,4 +360,11 @@ int vamla_slot_gather(const uint16_t* kv_pool, const int32_t* idx, int64_t n, ui
                                                                                      : VAMLA_ERR_LAUNCH;
 }
 
+int vamla_read_rows(const uint16_t* kv_pool, const int32_t* idx, int64_t n, uint32_t* sink, void* stream) {
+  if (n < 0 || !kv_pool || !sink || (n > 0 && !idx)) return VAMLA_ERR_INVALID_ARG;
+  const int st = check_arch();
+  if (st != VAMLA_OK) return st;
+  return launch_read_rows(kv_pool, idx, n, sink, (hipStream_t)stream) == hipSuccess ? VAMLA_OK : VAMLA_ERR_LAUNCH;
+}
+
 }  // extern "C"

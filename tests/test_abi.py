@@ -179,6 +179,14 @@ def test_slot_gather_empty_is_a_noop(L):
     assert L.vamla_slot_gather(None, None, -1, None, None) == -1
 
 
+def test_read_rows_argument_checks(L):
+    # refused before any HIP call: negative count, null pool or sink, null idx with rows
+    assert L.vamla_read_rows(None, None, -1, None, None) == -1
+    assert L.vamla_read_rows(None, 16, 4, 16, None) == -1
+    assert L.vamla_read_rows(16, 16, 4, None, None) == -1
+    assert L.vamla_read_rows(16, None, 4, 16, None) == -1
+
+
 def _valid_case():
     x = gen.config_inputs(1)
     p = vb.Problem.from_host(x.cu_prefix, x.cu_tree, 16, x.pool.shape[0], gen.SOFTMAX_SCALE)

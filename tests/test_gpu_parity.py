@@ -358,6 +358,23 @@ def test_slot_gather_bit_exact():
                           vo.gather_rows(x.pool, [5, 5, 1, 32767, 9, 9, 9]))
 
 
+def test_read_rows_checksum():
+    # the XOR of the sink words equals the XOR of every 32-bit word of the
+    # rows named, for a workload's prefix, a ragged repeated list and none
+    import torch
+    x = gen.config_inputs(2, slot_mode="scrambled")
+    d = to_dev(x)
+    words = lambda rows: np.bitwise_xor.reduce(np.ascontiguousarray(rows).view(np.uint32), axis=None)
+    for idx_h in (x.prefix_slot_idx, np.array([5, 5, 1, 32767, 9, 9, 9], np.int32)):
+        sink = vb.read_rows(d["kv_pool"], torch.from_numpy(np.ascontiguousarray(idx_h, np.int32)).cuda())
+        torch.cuda.synchronize()
+        got = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32))
+        assert got == words(vo.gather_rows(x.pool, idx_h)), len(idx_h)
+    sink = vb.read_rows(d["kv_pool"], torch.zeros(0, dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    assert not sink.cpu().numpy().any()
+
+
 def test_defragmented_pool_gives_identical_result():
     import torch
     x = gen.config_inputs(2, slot_mode="scrambled")
