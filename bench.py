@@ -162,6 +162,33 @@ def time_events(fn, iters: int) -> float:
     return s.elapsed_time(e) / iters
 
 
+def time_graph(fn, iters: int) -> float:
+    """Average ms per call of fn, from one captured graph of iters calls
+    replayed between events: no host launch overhead between the calls, for
+    kernels short enough that the binding's per-call host work would
+    otherwise set the pace."""
+    import torch
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn(0)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(iters):
+            fn(i)
+    g.replay()
+    torch.cuda.synchronize()
+    s = torch.cuda.Event(enable_timing=True)
+    e = torch.cuda.Event(enable_timing=True)
+    s.record()
+    g.replay()
+    e.record()
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) / iters
+
+
 def time_after(first, second, iters: int) -> float:
     """Average ms of second(i) when it follows first(i) on the launch stream,
     from an event pair around second alone: a short kernel timed back to back
@@ -411,11 +438,13 @@ def main():
         err(f"[bench] per-step us p10/p50/p90: {pct} (pool copies rotated), {warm} (one pool copy, warm); "
             f"device copy {copy_gbs:.0f} GB/s")
         # the same rows read and nothing else (vamla_read_rows): the rate a
-        # scattered read of this step's KV rows reaches on this chip
+        # scattered read of this step's KV rows reaches on this chip (timed
+        # from a captured graph: a short kernel behind the binding's host
+        # work would otherwise time the host)
         rows_all = torch.cat([pre[:x.total_prefix], tre])
         sink = torch.empty(vb.READ_ROWS_SINK_WORDS, dtype=torch.int32, device=dev)
         vb.read_rows(pools[0], rows_all, sink)   # first launch of the kernel loads its code object
-        ms_read = time_events(lambda i: vb.read_rows(pools[i % n_copies], rows_all, sink), iters)
+        ms_read = time_graph(lambda i: vb.read_rows(pools[i % n_copies], rows_all, sink), iters)
         read_ceiling = {"us": round(ms_read * 1e3, 2),
                         "gbs": round(alg["kv_bytes"] / (ms_read * 1e-3) / 1e9, 1),
                         "split_us_over_read_us": round(ms_read / ms_split, 4),
