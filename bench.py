@@ -256,6 +256,8 @@ def main():
     ap.add_argument("--std-q", type=float, default=0.1,
                     help="standard deviation of the query values (0.1: score sd ~0.017 nats; 17.3: ~3 nats, a "
                          "realistic logit spread)")
+    ap.add_argument("--chunk", type=int, default=0,
+                    help="prefix keys per work item (a multiple of 32); 0 = the planner's choice")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--warm-seconds", type=float, default=WARM_SECONDS,
                     help="after the --warmup steps, keep stepping until this much wall time has passed "
@@ -282,7 +284,9 @@ def main():
         (f", query sd {args.std_q} (score sd {args.std_q * 0.1 * 24 * x.scale:.2f} nats)" if args.std_q != 0.1 else "")
     err(f"[bench] workload: {wname}  (inputs generated in {time.perf_counter() - t0:.1f} s)")
     alg = algorithmic(x)
-    prob = vb.Problem.from_host(x.cu_prefix, x.cu_tree, x.num_heads, x.pool.shape[0], x.scale)
+    prob = vb.Problem.from_host(x.cu_prefix, x.cu_tree, x.num_heads, x.pool.shape[0], x.scale, chunk=args.chunk)
+    if args.chunk:
+        wname += f", {args.chunk}-key chunks"
     if args.device_lengths:
         prob.flags = vb.FLAG_DEVICE_LENGTHS
         wname += ", lengths read on the device"
@@ -318,7 +322,7 @@ def main():
         dst = torch.empty((n_rows, 576), dtype=torch.bfloat16, device=dev)
         pre_c = torch.arange(0, max(x.total_prefix, 1), dtype=torch.int32, device=dev)
         tre_c = torch.arange(x.total_prefix, n_rows, dtype=torch.int32, device=dev)
-        prob_c = vb.Problem.from_host(x.cu_prefix, x.cu_tree, x.num_heads, n_rows, x.scale)
+        prob_c = vb.Problem.from_host(x.cu_prefix, x.cu_tree, x.num_heads, n_rows, x.scale, chunk=args.chunk)
         prob_c.flags = prob.flags
         ws_c = vb.Workspace(prob_c)
 

@@ -33,6 +33,12 @@ constexpr int64_t kItemOverheadKeys = 256;
 // Cost of one item's partial (64 rows x 2 KB written by the split pass and
 // read back by the merge) at the chip's write + read rate, in the same units.
 constexpr int64_t kPartialKeys = 2;
+// Requests of at most 16 query rows (decode) are bound by reading the KV
+// rows from HBM, and the chip serves their scattered rows faster with fewer
+// concurrent streams: on the 128k-key decode step, 205 items of 640 keys ran
+// 3% faster than 241 items of 544 keys, 171 items of 768 keys 2% faster and
+// 128 items of 1024 keys 7% slower.  Their plans keep to this many items.
+constexpr int64_t kHbmBoundItems = 208;
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
@@ -60,7 +66,7 @@ int check_shape(const vamla_params* p) {
   return VAMLA_OK;
 }
 
-int64_t choose_chunk(const vamla_params* p, int64_t row_tiles) {
+int64_t choose_chunk(const vamla_params* p, int64_t row_tiles, int64_t rows) {
   if (p->chunk > 0) return p->chunk;
   const int64_t maxL = p->max_prefix;
   if (maxL <= VAMLA_KEY_TILE) return VAMLA_KEY_TILE;
@@ -83,6 +89,9 @@ int64_t choose_chunk(const vamla_params* p, int64_t row_tiles) {
     const int64_t chunks =
         std::min<int64_t>(ceil_div(total, c) + ceil_div(p->batch - 1, 2), (int64_t)p->batch * ceil_div(maxL, c));
     const int64_t items = row_tiles * chunks;
+    // HBM-bound plans skip chunk sizes with more items than the knee (the
+    // largest candidate, one chunk per request, always stays)
+    if (rows <= 16 && items > kHbmBoundItems && k > 1) continue;
     const int64_t rounds = ceil_div(items, kCUs);
     const int64_t last = maxL - (ceil_div(maxL, c) - 1) * c;
     const int64_t item_keys = std::max(c, ceil_div(last, VAMLA_KEY_TILE) * VAMLA_KEY_TILE + tree_keys);
@@ -102,7 +111,7 @@ int make_plan(const vamla_params* p, vamla_plan_info* out) {
   std::memset(&pl, 0, sizeof(pl));
   const int64_t rows = (int64_t)p->max_tree * p->num_heads;
   const int64_t row_tiles = ceil_div(rows, kRowTile);
-  const int64_t chunk = choose_chunk(p, row_tiles);
+  const int64_t chunk = choose_chunk(p, row_tiles, rows);
   const int64_t max_chunks = std::max<int64_t>(1, ceil_div(p->max_prefix, chunk));
   const int64_t items = (int64_t)p->batch * row_tiles * max_chunks;
   if (items > (int64_t)INT32_MAX / 2) return VAMLA_ERR_UNSUPPORTED;

@@ -61,6 +61,17 @@ def prob(k):
     return table[k]
 
 
+def test_hbm_bound_plans_keep_to_the_item_knee(L):
+    # requests of <= 16 rows (decode) keep to 208 work items; 17 rows and up
+    # are planned as before
+    for prefix in (32768, 65536, 131072, 185000, 1 << 20):
+        for heads in (1, 8, 16):
+            info = vb.plan(vb.Problem(1, heads, 1 << 21, gen.SOFTMAX_SCALE, 1, 1, prefix, prefix))
+            assert info.max_chunks <= 208, (prefix, heads, info.max_chunks)
+    assert vb.plan(prob(6)).chunk == 640
+    assert vb.plan(prob(7)).max_chunks * vb.plan(prob(7)).row_tiles > 208
+
+
 @pytest.mark.parametrize("k", [1, 2, 3, 4, 5, 6, 7])
 def test_plan_covers_the_problem(L, k):
     p = prob(k)
