@@ -43,17 +43,20 @@ from speculative_decoding_tree_verify_amd import inputs as gen  # noqa: E402
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
 
-# HBM bytes per launch of the split kernel on the default workload, from two
-# rocprofv3 --pmc passes (FETCH_SIZE, WRITE_SIZE; summary under profiles/),
-# each scaled by what the counter reads for a plain device copy of known size
+# HBM bytes per launch of the split kernel on a workload, from two rocprofv3
+# --pmc passes (FETCH_SIZE, WRITE_SIZE; summaries under profiles/), each
+# scaled by what the counter reads for a plain device copy of known size
 # (FETCH_SIZE reports half of the bytes a copy reads, WRITE_SIZE all it
-# writes).  Valid only for the kernel sources they were taken on: keyed by
-# their sha256, and reported as null for any other build.
+# writes).  Valid only for the sources they were taken on (the kernel and the
+# planner, which fixes the chunking): keyed by their sha256 and the workload,
+# and reported as null for any other build, workload or layout override.
 MEASURED_TRAFFIC = {
-    # sha256(prefix_splitkv.hip + kernels.h): (fetch KiB, write KiB, fetch scale, write scale)
-    "895e90703575b71dc248e557d62dc2f447742b429e59cac5e2458298b0df3a0f": (59335.0, 31260.9, 2.0, 1.0),
+    # (sha256(prefix_splitkv.hip + kernels.h + vamla.cpp), workload):
+    #     (fetch KiB, write KiB, fetch scale, write scale)
+    ("58b5924942a21d3d0a9c1ba7578cb72acf944740752988c0ac6b6fad25efaaa4", 3): (59328.1, 31260.9, 2.0, 1.0),
+    ("58b5924942a21d3d0a9c1ba7578cb72acf944740752988c0ac6b6fad25efaaa4", 6): (74219.8, 6572.8, 2.0, 1.0),
 }
-KERNEL_SOURCES = ("prefix_splitkv.hip", "kernels.h")
+KERNEL_SOURCES = ("prefix_splitkv.hip", "kernels.h", "vamla.cpp")
 KV_ROW_BYTES = 576 * 2
 FLOPS_PER_ROW_KEY = 2 * (576 + 512)
 POOL_ROTATION_BYTES = 768 << 20   # > 3x the Infinity Cache
@@ -101,13 +104,17 @@ def algorithmic(x: gen.VerifyInputs):
                 io_bytes=io_bytes, split_bytes=kv_rows * KV_ROW_BYTES + T * H * KV_ROW_BYTES)
 
 
-def split_kernel_traffic():
+def kernel_sources_hash() -> str:
     import hashlib
     h = hashlib.sha256()
     for name in KERNEL_SOURCES:
         with open(os.path.join(ROOT, "speculative_decoding_tree_verify_amd", "csrc", name), "rb") as f:
             h.update(f.read())
-    m = MEASURED_TRAFFIC.get(h.hexdigest())
+    return h.hexdigest()
+
+
+def split_kernel_traffic(config: int):
+    m = MEASURED_TRAFFIC.get((kernel_sources_hash(), config))
     if m is None:
         return None
     fetch_kib, write_kib, fs, ws = m
@@ -519,7 +526,8 @@ def main():
             "defrag_us": defrag_us,
         },
         "roofline": roofline_of_split(t_mfma >= t_hbm, flops, alg, ms_split,
-                                      split_kernel_traffic() if args.config == 3 and not args.slot_mode else None),
+                                      None if (args.slot_mode or args.chunk or args.defrag)
+                                      else split_kernel_traffic(args.config)),
         "cpu_baseline": ({k: v for k, v in cpu.items() if k != "ms_per_step"} if cpu else None),
     }
     print(json.dumps(rec), flush=True)
