@@ -288,6 +288,19 @@ def test_small_rows_decode_full():
     check(x, what="decode 16 rows, 131072-token prefix")
 
 
+def test_small_rows_decode_batch():
+    # four decode requests (one node each, 16 heads) with unequal long
+    # prefixes in one churned pool: the plan keeps to the HBM-bound item cap
+    # (fewer, longer chunks) and the merge folds each request's own chunks
+    rng = np.random.default_rng(77)
+    lens = [131072, 70001, 33000, 5]
+    x = small(lens, [np.array([-1], np.int32)] * 4, 16, seed=78, pool=1 << 19, mode="churned")
+    info = vb.plan(problem(x))
+    log(f"[case] decode batch {lens}: chunk {info.chunk}, {info.max_chunks} chunks per request")
+    assert info.max_chunks <= 208
+    check(x, what="decode batch of four")
+
+
 def test_small_rows_nine_queries_full():
     x = gen.config_inputs(7)
     check(x, what="9 nodes x 16 heads, 185000-token prefix")
