@@ -265,6 +265,9 @@ def main():
                          "realistic logit spread)")
     ap.add_argument("--chunk", type=int, default=0,
                     help="prefix keys per work item (a multiple of 32); 0 = the planner's choice")
+    ap.add_argument("--gemm-ref", action="store_true",
+                    help="also time the vendor library's bf16 GEMMs of the same two shapes (Q.K^T and P.V, "
+                         "single request, rows contiguous, no softmax): context for the split kernel's rate")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--warm-seconds", type=float, default=WARM_SECONDS,
                     help="after the --warmup steps, keep stepping until this much wall time has passed "
@@ -475,6 +478,33 @@ def main():
     err(f"[bench] roofline bounds per step: MFMA {t_mfma * 1e6:.1f} us, HBM {t_hbm * 1e6:.1f} us; "
         f"fraction of binding roofline {max(t_mfma, t_hbm) / (ms_per_step * 1e-3):.3f}")
 
+    gemm_ref = None
+    if args.gemm_ref and x.batch == 1:
+        # torch.matmul (hipBLASLt) on contiguous 2-D bf16 operands, fp32
+        # accumulation: rows x 576 times 576 x L, then rows x L times L x 512
+        rows_n, L_n = x.total_tree * x.num_heads, x.total_prefix
+        g = torch.Generator(device=dev).manual_seed(5)
+        qa = (torch.randn(rows_n, 576, device=dev, generator=g) * 0.1).to(torch.bfloat16)
+        kt = (torch.randn(576, L_n, device=dev, generator=g) * 0.1).to(torch.bfloat16).contiguous()
+        pa = (torch.rand(rows_n, L_n, device=dev, generator=g)).to(torch.bfloat16)
+        vb_ = (torch.randn(L_n, 512, device=dev, generator=g) * 0.1).to(torch.bfloat16).contiguous()
+        for _ in range(3):   # the library's first calls load and select its kernels
+            torch.matmul(qa, kt)
+            torch.matmul(pa, vb_)
+        torch.cuda.synchronize()
+        ms_qk = time_events(lambda i: torch.matmul(qa, kt), iters)
+        ms_pv = time_events(lambda i: torch.matmul(pa, vb_), iters)
+        f_qk, f_pv = 2.0 * rows_n * 576 * L_n, 2.0 * rows_n * L_n * 512
+        gemm_ref = {"qk_us": round(ms_qk * 1e3, 2), "pv_us": round(ms_pv * 1e3, 2),
+                    "sum_us": round((ms_qk + ms_pv) * 1e3, 2),
+                    "qk_tflops": round(f_qk / (ms_qk * 1e-3) / 1e12, 1),
+                    "pv_tflops": round(f_pv / (ms_pv * 1e-3) / 1e12, 1),
+                    "split_us_over_sum": round((ms_qk + ms_pv) / ms_split, 4)}
+        err(f"[bench] vendor GEMMs of the same shapes: Q.K^T {ms_qk * 1e3:.1f} us ({gemm_ref['qk_tflops']} TFLOP/s), "
+            f"P.V {ms_pv * 1e3:.1f} us ({gemm_ref['pv_tflops']} TFLOP/s); sum {gemm_ref['sum_us']} us against "
+            f"the split kernel's {ms_split * 1e3:.1f} us")
+        del qa, kt, pa, vb_
+
     if args.calib_copy:
         a = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
         b = torch.empty_like(a)
@@ -522,6 +552,7 @@ def main():
             "step_us_warm_p10_p50_p90": warm,
             "device_copy_gbs": round(copy_gbs, 1) if copy_gbs else None,
             "kv_read_ceiling": read_ceiling,
+            "vendor_gemm_same_shapes": gemm_ref,
             "pct_of_device_copy": round(value / copy_gbs * 100, 3) if copy_gbs else None,
             "defrag_us": defrag_us,
         },
