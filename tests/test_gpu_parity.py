@@ -125,6 +125,21 @@ def test_all_128_heads():
     check(x, chunk=128, what="H=128")
 
 
+def test_zero_queries_average_the_visible_values():
+    # every score is 0, so each row's weights are uniform over its visible
+    # keys (the prefix plus its ancestors-or-self): out is their mean V and
+    # lse = ln(count).  The split kernel's reference then sits 40 log2 units
+    # above every score, so each weight is 2^-40 before normalisation
+    rng = np.random.default_rng(9)
+    parent = gen.random_tree(9, rng)
+    x = small([3000], [parent], 4, seed=92)
+    x.q[:] = 0
+    out, lse = check(x, chunk=1024, what="zero queries")
+    depth = gen.tree_depths(parent)
+    want = np.log(3000 + depth + 1.0)
+    np.testing.assert_allclose(lse, np.repeat(want[:, None], 4, axis=1), atol=1e-4)
+
+
 def test_sharp_scores_move_the_reference():
     rng = np.random.default_rng(6)
     x = small([3000], [gen.random_tree(9, rng)], 4, seed=18, std_q=10.0)              # score sd ~ 1.7
