@@ -53,6 +53,8 @@ def assert_close_out(got, ref, what=""):
     err = np.abs(got - ref)
     scale = np.abs(ref).max()
     assert np.all(np.isfinite(got)), f"{what}: non-finite output"
+    tol = min(1e-2, 1e-2 * scale + 1e-6)
+    log(f"[margin] {what}: out max abs err {err.max():.3e} = {err.max() / tol:.3f} of the tolerance")
     assert err.max() <= 1e-2, f"{what}: max abs err {err.max():.3e}"
     assert err.max() <= 1e-2 * scale + 1e-6, f"{what}: max abs err {err.max():.3e} vs 1e-2*max|ref|={1e-2 * scale:.3e}"
 
@@ -60,4 +62,5 @@ def assert_close_out(got, ref, what=""):
 def assert_close_lse(got, ref, what=""):
     err = np.abs(got - ref)
     assert np.all(np.isfinite(got)), f"{what}: non-finite lse"
+    log(f"[margin] {what}: lse max abs err {err.max():.3e} = {err.max() / 1e-3:.3f} of the tolerance")
     assert err.max() <= 1e-3, f"{what}: lse max abs err {err.max():.3e}"
