@@ -263,6 +263,8 @@ def main():
     ap.add_argument("--std-q", type=float, default=0.1,
                     help="standard deviation of the query values (0.1: score sd ~0.017 nats; 17.3: ~3 nats, a "
                          "realistic logit spread)")
+    ap.add_argument("--prefix", type=int, default=None,
+                    help="prefix length for a single-request workload (the tree, heads and pool stay the workload's)")
     ap.add_argument("--chunk", type=int, default=0,
                     help="prefix keys per work item (a multiple of 32); 0 = the planner's choice")
     ap.add_argument("--gemm-ref", action="store_true",
@@ -288,10 +290,11 @@ def main():
     vb.lib()   # fail loudly if the HIP library is missing
 
     t0 = time.perf_counter()
-    x = gen.config_inputs(args.config, slot_mode=args.slot_mode, std_q=args.std_q)
+    x = gen.config_inputs(args.config, slot_mode=args.slot_mode, std_q=args.std_q, prefix=args.prefix)
     wname = workload_name(args.config) + (f", {args.slot_mode} slots" if args.slot_mode else "") + \
         (", graph replay" if args.launch == "graph" else "") + \
-        (f", query sd {args.std_q} (score sd {args.std_q * 0.1 * 24 * x.scale:.2f} nats)" if args.std_q != 0.1 else "")
+        (f", query sd {args.std_q} (score sd {args.std_q * 0.1 * 24 * x.scale:.2f} nats)" if args.std_q != 0.1 else "") + \
+        (f", prefix {args.prefix} tokens" if args.prefix is not None else "")
     err(f"[bench] workload: {wname}  (inputs generated in {time.perf_counter() - t0:.1f} s)")
     alg = algorithmic(x)
     prob = vb.Problem.from_host(x.cu_prefix, x.cu_tree, x.num_heads, x.pool.shape[0], x.scale, chunk=args.chunk)
@@ -302,7 +305,8 @@ def main():
         wname += ", lengths read on the device"
     info = vb.plan(prob)
     err(f"[bench] plan: chunk={info.chunk} row_tiles={info.row_tiles} chunks={info.max_chunks} "
-        f"grid={info.grid_items} workspace={info.workspace_bytes / 1e6:.1f} MB")
+        f"grid={info.grid_items} workspace={info.workspace_bytes / 1e6:.1f} MB"
+        + (" (one chunk per request: one launch, the split pass writes the output)" if info.max_chunks == 1 else ""))
 
     dev = "cuda"
     bf = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
@@ -371,8 +375,13 @@ def main():
             graphs[i % n_copies].replay()
         err(f"[bench] launch: {n_copies} captured graph(s), one verify step each")
 
+    one_launch = info.max_chunks == 1
+
     def split_only(i):
-        vb.split_partials(prob, q, pools[i % n_copies], pre, tre, par, cup, cut, ws)
+        if one_launch:   # the step is the split pass alone, writing the output itself
+            vb.verify_attn_mla(prob, q, pools[i % n_copies], pre, tre, par, cup, cut, ws=ws, out=out, lse=lse)
+        else:
+            vb.split_partials(prob, q, pools[i % n_copies], pre, tre, par, cup, cut, ws)
 
     def merge_only(i):
         vb.lse_merge(prob, cup, cut, ws, out, lse)
@@ -442,7 +451,7 @@ def main():
             break
     ms_split = split_passes[-1]
     err(f"[bench] split kernel timing passes (us): {[round(v * 1e3, 1) for v in split_passes]}")
-    ms_merge = time_after(split_only, merge_only, iters)
+    ms_merge = 0.0 if one_launch else time_after(split_only, merge_only, iters)
     ms_step_ev = time_events(step, iters)
     pct = warm = copy_gbs = read_ceiling = None
     if not args.calib_copy:   # counter runs keep to the copies they calibrate against
@@ -522,7 +531,8 @@ def main():
         err(f"[bench] cpu oracle: {cpu['ms_per_step']:.1f} ms/step on {cpu['cores']} threads")
 
     rec = {
-        "metric": "effective KV-read GB/s (% HBM peak) + us per verify step, " + METRIC_WORKLOAD.get(args.config, wname),
+        "metric": "effective KV-read GB/s (% HBM peak) + us per verify step, " +
+                  (wname if args.prefix is not None else METRIC_WORKLOAD.get(args.config, wname)),
         "value": round(value, 2),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -540,7 +550,9 @@ def main():
             "pool_slots": int(x.pool.shape[0]), "kv_bytes": alg["kv_bytes"],
             "us_per_step": round(ms_per_step * 1e3, 2),
             "pct_hbm_peak": round(value / HBM_PEAK_GBS * 100, 3),
-            "kernel_us": {"prefix_splitkv": round(ms_split * 1e3, 2), "lse_merge": round(ms_merge * 1e3, 2)},
+            "kernel_us": {"prefix_splitkv": round(ms_split * 1e3, 2),
+                          "lse_merge": None if one_launch else round(ms_merge * 1e3, 2)},
+            "launches_per_step": 1 if one_launch else 2,
             "prefix_splitkv_us_first_pass": round(split_passes[0] * 1e3, 2),
             "prefix_splitkv_timing_passes": len(split_passes),
             "warmup_steps_run": n_warm,
@@ -557,7 +569,7 @@ def main():
             "defrag_us": defrag_us,
         },
         "roofline": roofline_of_split(t_mfma >= t_hbm, flops, alg, ms_split,
-                                      None if (args.slot_mode or args.chunk or args.defrag)
+                                      None if (args.slot_mode or args.chunk or args.defrag or args.prefix is not None)
                                       else split_kernel_traffic(args.config)),
         "cpu_baseline": ({k: v for k, v in cpu.items() if k != "ms_per_step"} if cpu else None),
     }

@@ -218,7 +218,14 @@ int vamla_validate(const vamla_params* p, const int32_t* h_parent, const int32_t
 /*
  * The verify step: the split pass (prefix chunks; the last chunk of each
  * request also takes its tree keys under the ancestor mask) and the LSE merge,
- * two kernels enqueued on `stream`.
+ * two kernels enqueued on `stream`.  When the plan has one chunk per request
+ * (vamla_plan_info.max_chunks == 1: the planner's choice for short prefixes,
+ * or an explicit chunk at least max_prefix) the split pass writes out and lse
+ * itself and the step is a single launch, with the same bits the two launches
+ * would give (a merge of one partial multiplies it by exactly 1); the
+ * workspace's partial region is then left untouched.  The pages name short
+ * prefixes as where a launch-bound custom kernel lost ("The Architecture
+ * Detective ...", "Context: The Performance Crisis").
  *   q               device bf16 [T, H, 576]: queries of every node (RoPE applied)
  *   kv_pool         device bf16 [P, 576]: latent rows; V = first 512 columns
  *   prefix_slot_idx device int32 [total_prefix]: pool slot of each prefix token

@@ -39,6 +39,8 @@ struct PrefixArgs {
   float scale_log2;           // softmax_scale * log2(e)
   int32_t device_lengths;     // 1: lengths from cu_* only, chunk from device_chunk()
   const int32_t* debug_record; // non-null with VAMLA_FLAG_DEBUG_VALIDATE: no work if record[0] != 0
+  uint16_t* out;              // non-null when every request is one chunk: the final out [T, H, 512]
+  float* lse;                 // and lse [T, H] are written here instead of partials (no merge)
 };
 
 // LSE merge of the chunk partials.

@@ -236,8 +236,20 @@ __global__ __launch_bounds__(512, 1) void prefix_splitkv_kernel(PrefixArgs a) {
   static_assert(kRing == 4, "ring slots are picked by the low two bits of the tile index");
   auto ring = [&](int i) -> uint8_t* { i &= kRing - 1; return i == 0 ? tile0 : i == 1 ? tile1 : i == 2 ? tile2 : tile3; };
 
-  // with the debug flag, a failed device-side index check leaves no work
-  if (a.debug_record && __builtin_amdgcn_readfirstlane(a.debug_record[0]) != 0) return;
+  // with the debug flag, a failed device-side index check leaves no work;
+  // when this pass writes the final output (one chunk per request), every
+  // element of it is NaN instead, as the merge would make it
+  if (a.debug_record && __builtin_amdgcn_readfirstlane(a.debug_record[0]) != 0) {
+    if (a.out) {
+      const int64_t rows = (int64_t)a.total_tree * a.num_heads;
+      const int64_t nthreads = (int64_t)gridDim.x * blockDim.x;
+      const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+      const uint2 nan2 = make_uint2(0x7FC07FC0u, 0x7FC07FC0u);
+      for (int64_t i = gid; i < rows * (kDv / 4); i += nthreads) *(uint2*)(a.out + i * 4) = nan2;
+      for (int64_t i = gid; i < rows; i += nthreads) a.lse[i] = __builtin_nanf("");
+    }
+    return;
+  }
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const bool is_qk = w < 4;
@@ -528,7 +540,11 @@ __global__ __launch_bounds__(512, 1) void prefix_splitkv_kernel(PrefixArgs a) {
       const int j = 32 * pr + lane;
       const float l = sh.mtl[0][w][lane].x + sh.mtl[0][w ^ 1][lane].x;
       sh.rowl[j] = l;
-      if (tile * kRowTile + j < rows_b) a.part_lse[pidx * kRowTile + j] = m_ref[q4] * kLn2 + logf(l);
+      if (tile * kRowTile + j < rows_b) {
+        const float v = m_ref[q4] * kLn2 + logf(l);
+        if (a.out) a.lse[(size_t)t0 * a.num_heads + tile * kRowTile + j] = v;   // the request's only chunk
+        else a.part_lse[pidx * kRowTile + j] = v;
+      }
     }
     lds_barrier();
     return;
@@ -678,6 +694,9 @@ __global__ __launch_bounds__(512, 1) void prefix_splitkv_kernel(PrefixArgs a) {
     const int rit = 32 * rb + (lane & 31);
     if (tile * kRowTile + rit >= rows_b) continue;
     const float inv = __builtin_amdgcn_rcpf(sh.rowl[rit]);   // <= 1 ulp
+    // the request's only chunk: its normalised partial is the output (a
+    // merge of one partial multiplies it by exactly 1), rounded to bf16
+    uint16_t* orow = a.out ? a.out + ((size_t)t0 * a.num_heads + tile * kRowTile + rit) * kDv : nullptr;
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb) {
 #pragma unroll
@@ -686,7 +705,16 @@ __global__ __launch_bounds__(512, 1) void prefix_splitkv_kernel(PrefixArgs a) {
         const f32x16& acc = o[cb + 4 * rb];
         const float4 v = make_float4(acc[4 * rq] * inv, acc[4 * rq + 1] * inv, acc[4 * rq + 2] * inv,
                                      acc[4 * rq + 3] * inv);
-        *(float4*)(po + ((size_t)d4 * kRowTile + rit) * 4) = v;
+        if (orow) {
+          uint2 pk;
+          pk.x = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v.x) |
+                 ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v.y) << 16);
+          pk.y = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v.z) |
+                 ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v.w) << 16);
+          *(uint2*)(orow + d4 * 4) = pk;
+        } else {
+          *(float4*)(po + ((size_t)d4 * kRowTile + rit) * 4) = v;
+        }
       }
     }
   }

@@ -39,6 +39,14 @@ constexpr int64_t kPartialKeys = 2;
 // 3% faster than 241 items of 544 keys, 171 items of 768 keys 2% faster and
 // 128 items of 1024 keys 7% slower.  Their plans keep to this many items.
 constexpr int64_t kHbmBoundItems = 208;
+// What the merge launch costs a short step beyond the work it takes off the
+// split pass, in keys of streaming work.  A plan with one chunk per request
+// skips it: the split pass writes the output itself.  Fitted to the measured
+// crossover on 9- and 65-node trees of 16 heads: one launch is faster at
+// 64-key prefixes (14.4 against 15.1 us, 16.9 against 18.3 us), ties at 128
+// keys with 65 nodes and is slower from 128 keys with 9 nodes (16.4 against
+// 15.3 us), which bounds this cost to 20..72 keys.
+constexpr int64_t kMergeKeys = 48;
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
@@ -95,7 +103,8 @@ int64_t choose_chunk(const vamla_params* p, int64_t row_tiles, int64_t rows) {
     const int64_t rounds = ceil_div(items, kCUs);
     const int64_t last = maxL - (ceil_div(maxL, c) - 1) * c;
     const int64_t item_keys = std::max(c, ceil_div(last, VAMLA_KEY_TILE) * VAMLA_KEY_TILE + tree_keys);
-    const int64_t cost = rounds * (item_keys + kItemOverheadKeys) + items * kPartialKeys;
+    const int64_t cost =
+        rounds * (item_keys + kItemOverheadKeys) + (c >= maxL ? 0 : items * kPartialKeys + kMergeKeys);
     if (cost < best_cost || (cost == best_cost && c > best_c)) {   // ties: larger chunk, fewer partials
       best_cost = cost;
       best_c = c;
@@ -182,7 +191,7 @@ int validate_launch(const vamla_params* p, const vamla_plan_info& pl, const int3
 
 int split_launch(const vamla_params* p, const vamla_plan_info& pl, const uint16_t* q, const uint16_t* pool,
                  const int32_t* prefix_slot_idx, const int32_t* tree_slot_idx, const int32_t* parent,
-                 hipStream_t stream) {
+                 uint16_t* out, float* lse, hipStream_t stream) {
   PrefixArgs a;
   a.q = q;
   a.pool = pool;
@@ -204,6 +213,8 @@ int split_launch(const vamla_params* p, const vamla_plan_info& pl, const uint16_
   a.scale_log2 = p->softmax_scale * 1.4426950408889634f;
   a.device_lengths = (p->flags & VAMLA_FLAG_DEVICE_LENGTHS) ? 1 : 0;
   a.debug_record = debug_record(p, pl);
+  a.out = out;
+  a.lse = lse;
   if (a.debug_record) {
     const int st = validate_launch(p, pl, prefix_slot_idx, tree_slot_idx, parent, stream);
     if (st != VAMLA_OK) return st;
@@ -335,7 +346,10 @@ int verify_attn_mla(const vamla_params* p, const uint16_t* q, const uint16_t* kv
   if (!q || !kv_pool || !tree_slot_idx || !parent || !out || !lse) return VAMLA_ERR_INVALID_ARG;
   if (p->total_prefix > 0 && !prefix_slot_idx) return VAMLA_ERR_INVALID_ARG;
   hipStream_t s = (hipStream_t)stream;
-  st = split_launch(p, pl, q, kv_pool, prefix_slot_idx, tree_slot_idx, parent, s);
+  // one chunk per request: the split pass writes out and lse itself and the
+  // step is a single launch (the merge of one partial is the identity)
+  if (pl.max_chunks == 1) return split_launch(p, pl, q, kv_pool, prefix_slot_idx, tree_slot_idx, parent, out, lse, s);
+  st = split_launch(p, pl, q, kv_pool, prefix_slot_idx, tree_slot_idx, parent, nullptr, nullptr, s);
   if (st != VAMLA_OK) return st;
   return merge_launch(p, pl, out, lse, s);
 }
@@ -348,7 +362,8 @@ int vamla_split_partials(const vamla_params* p, const uint16_t* q, const uint16_
   if (st != VAMLA_OK) return st;
   if (!q || !kv_pool || !tree_slot_idx || !parent) return VAMLA_ERR_INVALID_ARG;
   if (p->total_prefix > 0 && !prefix_slot_idx) return VAMLA_ERR_INVALID_ARG;
-  return split_launch(p, pl, q, kv_pool, prefix_slot_idx, tree_slot_idx, parent, (hipStream_t)stream);
+  return split_launch(p, pl, q, kv_pool, prefix_slot_idx, tree_slot_idx, parent, nullptr, nullptr,
+                      (hipStream_t)stream);
 }
 
 int vamla_lse_merge(const vamla_params* p, uint16_t* out, float* lse, void* stream) {

@@ -303,21 +303,26 @@ CONFIG_NAMES = {
 
 
 def config_inputs(k: int, slot_mode: Optional[str] = None, std_q: float = 0.1,
-                  poison_unused: bool = True) -> VerifyInputs:
-    """Inputs of workload configuration k (1..7); seeds derive from 1000*k."""
+                  poison_unused: bool = True, prefix: Optional[int] = None) -> VerifyInputs:
+    """Inputs of workload configuration k (1..7); seeds derive from 1000*k.
+    prefix replaces the prefix length of a single-request workload (the tree,
+    heads, pool size and seeds stay those of workload k)."""
     seed = 1000 * k
     tree_rng = np.random.default_rng(np.random.SeedSequence(seed + 7))
+    if prefix is not None and (k == 5 or prefix < 0):
+        raise ValueError("prefix applies to the single-request workloads (1-4, 6, 7), as a length >= 0")
+    L = (lambda default: default if prefix is None else prefix)
     if k == 1:
-        return make_inputs([1024], [random_tree(9, tree_rng)], 16, 4096,
+        return make_inputs([L(1024)], [random_tree(9, tree_rng)], 16, max(4096, L(0) + 4096),
                            slot_mode or "scrambled", seed, std_q=std_q, poison_unused=poison_unused)
     if k == 2:
-        return make_inputs([8192], [chain_plus_branch()], 16, 32768,
+        return make_inputs([L(8192)], [chain_plus_branch()], 16, max(32768, L(0) + 4096),
                            slot_mode or "scrambled", seed, std_q=std_q, poison_unused=poison_unused)
     if k == 3:
-        return make_inputs([65536], [bounded_tree(65, tree_rng)], 16, 131072,
+        return make_inputs([L(65536)], [bounded_tree(65, tree_rng)], 16, max(131072, L(0) + 4096),
                            slot_mode or "scrambled", seed, std_q=std_q, poison_unused=poison_unused)
     if k == 4:
-        return make_inputs([131072], [bounded_tree(65, tree_rng)], 128, 1 << 20,
+        return make_inputs([L(131072)], [bounded_tree(65, tree_rng)], 128, max(1 << 20, L(0) + 4096),
                            slot_mode or "churned", seed, std_q=std_q, poison_unused=poison_unused)
     if k == 5:
         lens = [int(round(math.exp(tree_rng.uniform(math.log(4096), math.log(185000)))))
@@ -326,9 +331,9 @@ def config_inputs(k: int, slot_mode: Optional[str] = None, std_q: float = 0.1,
         return make_inputs(lens, trees, 16, 1 << 21, slot_mode or "churned", seed,
                            std_q=std_q, poison_unused=poison_unused)
     if k == 6:
-        return make_inputs([131072], [np.array([-1], np.int32)], 16, 1 << 18,
+        return make_inputs([L(131072)], [np.array([-1], np.int32)], 16, max(1 << 18, L(0) + 4096),
                            slot_mode or "scrambled", seed, std_q=std_q, poison_unused=poison_unused)
     if k == 7:
-        return make_inputs([185000], [chain_plus_branch()], 16, 1 << 18,
+        return make_inputs([L(185000)], [chain_plus_branch()], 16, max(1 << 18, L(0) + 4096),
                            slot_mode or "scrambled", seed, std_q=std_q, poison_unused=poison_unused)
     raise ValueError(k)

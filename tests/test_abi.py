@@ -102,7 +102,7 @@ def test_plan_fills_the_chip_for_the_64k_config(L):
 def _chunk_by_exhaustive_rule(p):
     """The chunk-size rule of the planner, evaluated over every k (the longest
     prefix split into k chunks), with the planner's cost constants."""
-    cus, overhead, partial, tile = 256, 256, 2, 32
+    cus, overhead, partial, tile, merge, hbm_items = 256, 256, 2, 32, 48, 208
     maxL = p.max_prefix
     if maxL <= tile:
         return tile
@@ -114,8 +114,12 @@ def _chunk_by_exhaustive_rule(p):
         c = -(-(-(-maxL // k)) // tile) * tile
         chunks = min(-(-total // c) + -(-(p.batch - 1) // 2), p.batch * -(-maxL // c))
         items = row_tiles * chunks
+        if p.max_tree * p.num_heads <= 16 and items > hbm_items and k > 1:
+            continue           # HBM-bound plans keep to the item knee
         last = maxL - (-(-maxL // c) - 1) * c
-        cost = -(-items // cus) * (max(c, -(-last // tile) * tile + tree_keys) + overhead) + items * partial
+        cost = -(-items // cus) * (max(c, -(-last // tile) * tile + tree_keys) + overhead)
+        if c < maxL:           # partials and the merge launch; one chunk writes the output itself
+            cost += items * partial + merge
         if best_cost is None or cost < best_cost or (cost == best_cost and c > best_c):
             best_c, best_cost = c, cost
     return best_c
@@ -125,6 +129,7 @@ def _chunk_by_exhaustive_rule(p):
     (1, 16, 65, 65536, 65536), (1, 128, 65, 131072, 131072), (8, 16, 33, 185000, 8 * 47500),
     (1, 16, 65, 4096, 4096), (64, 16, 65, 8192, 64 * 8192), (3, 16, 65, 100, 250), (1, 16, 1, 33, 33),
     (2, 128, 65, 1000003, 1500000), (5, 64, 17, 77777, 200000), (1, 16, 65, 300000, 300000),
+    (1, 16, 1, 131072, 131072), (4, 16, 1, 131072, 300000), (1, 16, 9, 150, 150), (1, 16, 9, 300, 300),
 ])
 def test_plan_chunk_matches_the_exhaustive_rule(L, batch, heads, max_tree, max_prefix, total_prefix):
     p = vb.Problem(batch, heads, 1 << 22, gen.SOFTMAX_SCALE, max_tree, max_tree * batch, max_prefix, total_prefix)

@@ -121,3 +121,20 @@ def test_a_valid_call_after_a_rejected_one_clears_the_record():
     o, l, rec, _ = _run(x, d, vb.FLAG_DEBUG_VALIDATE, ws=ws)
     assert rec == (0, 0, 0)
     assert np.isfinite(o.float().cpu().numpy()).all() and np.isfinite(l.cpu().numpy()).all()
+
+
+def test_one_launch_plan_writes_nan_on_a_bad_slot():
+    # short prefixes: one chunk per request, so the split pass writes the
+    # output itself; a failed check makes every element NaN there too
+    import torch
+    rng = np.random.default_rng(78)
+    x = gen.make_inputs([40, 12], [gen.random_tree(9, rng), gen.random_tree(5, rng)], 4, 256, "scrambled", seed=78)
+    p = vb.Problem.from_host(x.cu_prefix, x.cu_tree, x.num_heads, x.pool.shape[0], x.scale)
+    assert vb.plan(p).max_chunks == 1
+    d = _dev_with_spare_rows(x)
+    o0, l0, rec, _ = _run(x, d, vb.FLAG_DEBUG_VALIDATE)
+    assert rec == (0, 0, 0) and np.isfinite(o0.float().cpu().numpy()).all()
+    bad = d["prefix_slot_idx"].clone()
+    bad[45] = x.pool.shape[0] + 2
+    _expect_rejected(x, dict(d, prefix_slot_idx=bad), vb.FLAG_DEBUG_VALIDATE, (-7, 2, 45))
+    torch.cuda.synchronize()

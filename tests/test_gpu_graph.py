@@ -24,11 +24,17 @@ def _eager(p, d, ws):
     return out.clone(), lse.clone()
 
 
-@pytest.mark.parametrize("config", [1, 2])
+@pytest.mark.parametrize("config", [1, 2, 0])
 def test_captured_step_replays_bit_identical(config):
+    # 0: a 64-key prefix, whose plan is one chunk, so the captured step is a
+    # single launch (the split pass writes the output)
     import torch
     log(f"[case] graph capture, workload {config}")
-    x = gen.config_inputs(config)
+    if config:
+        x = gen.config_inputs(config)
+    else:
+        x = gen.make_inputs([64], [gen.random_tree(9, np.random.default_rng(5))], 16, 4096, "scrambled", 93)
+        assert vb.plan(problem(x)).max_chunks == 1
     d = to_dev(x)
     p = problem(x)
     ws_g = vb.Workspace(p)

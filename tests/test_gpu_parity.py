@@ -369,6 +369,36 @@ def test_stage_split_partials(lens, chunk):
             np.testing.assert_allclose(got_o, ro, atol=2e-3 * np.abs(ro).max() + 1e-6)
 
 
+@pytest.mark.parametrize("lens,N,H", [([64], 9, 16), ([0, 37, 64, 5], 5, 8), ([128], 65, 16), ([31], 33, 128)])
+def test_one_launch_for_single_chunk_plans(lens, N, H):
+    # short prefixes plan one chunk per request: the split pass writes out and
+    # lse itself (one launch).  A merge of one partial is the identity, so the
+    # result equals the two stage entry points' bit for bit on the same plan,
+    # and it meets the oracle
+    import torch
+    rng = np.random.default_rng(60 + N)
+    x = small(lens, [gen.random_tree(N, rng) for _ in lens], H, seed=61 + N)
+    p = problem(x)
+    info = vb.plan(p)
+    log(f"[case] one launch lens={lens} N={N} H={H}: chunk {info.chunk}, {info.max_chunks} chunk(s)")
+    assert info.max_chunks == 1
+    d = to_dev(x)
+    ws = vb.Workspace(p)
+    o1, l1 = vb.verify_attn_mla(p, d["q"], d["kv_pool"], d["prefix_slot_idx"], d["tree_slot_idx"], d["parent"],
+                                d["cu_prefix"], d["cu_tree"], ws=ws)
+    o2 = torch.full_like(o1, float("nan"))
+    l2 = torch.full_like(l1, float("nan"))
+    vb.split_partials(p, d["q"], d["kv_pool"], d["prefix_slot_idx"], d["tree_slot_idx"], d["parent"],
+                      d["cu_prefix"], d["cu_tree"], ws)
+    vb.lse_merge(p, d["cu_prefix"], d["cu_tree"], ws, o2, l2)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(l1.view(torch.int32), l2.view(torch.int32))
+    ro, rl = oracle_full(x)
+    assert_close_lse(l1.cpu().numpy().astype(np.float64), rl, "one launch")
+    assert_close_out(o1.float().cpu().numpy().astype(np.float64), ro, "one launch")
+
+
 def test_slot_gather_bit_exact():
     import torch
     x = gen.config_inputs(2, slot_mode="scrambled")
