@@ -53,8 +53,8 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
 MEASURED_TRAFFIC = {
     # (sha256(prefix_splitkv.hip + kernels.h + vamla.cpp), workload):
     #     (fetch KiB, write KiB, fetch scale, write scale)
-    ("58b5924942a21d3d0a9c1ba7578cb72acf944740752988c0ac6b6fad25efaaa4", 3): (59328.1, 31260.9, 2.0, 1.0),
-    ("58b5924942a21d3d0a9c1ba7578cb72acf944740752988c0ac6b6fad25efaaa4", 6): (74219.8, 6572.8, 2.0, 1.0),
+    ("830f552dfca411f26fae6011d8ece9414548b041f2254fb9c7ed56e36140a02f", 3): (59320.6, 31260.9, 2.0, 1.0),
+    ("830f552dfca411f26fae6011d8ece9414548b041f2254fb9c7ed56e36140a02f", 6): (74238.9, 6572.8, 2.0, 1.0),
 }
 KERNEL_SOURCES = ("prefix_splitkv.hip", "kernels.h", "vamla.cpp")
 KV_ROW_BYTES = 576 * 2
