@@ -89,6 +89,8 @@ def test_captured_step_replays_bit_identical(config):
 @pytest.mark.parametrize("cap,variants", [
     ([3000, 3000], [(3000, 3000), (1500, 2999), (0, 1), (700, 2), (3000, 0)]),
     ([5000], [(5000,), (1,), (0,), (2500,), (4097,)]),
+    # a one-chunk plan: the captured step is the split pass alone, writing out
+    ([60, 40], [(60, 40), (0, 1), (33, 0), (1, 40), (59, 39)]),
 ])
 def test_one_capture_serves_changing_prefix_lengths(cap, variants):
     # VAMLA_FLAG_DEVICE_LENGTHS: lengths are read from cu_prefix / cu_tree on
