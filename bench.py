@@ -10,18 +10,23 @@ step reads its KV rows from HBM rather than the 256 MB Infinity Cache.
 
 Prints ONE JSON line (stdout):
   value        effective KV-read bandwidth = unique KV bytes / step time (GB/s)
-  roofline     the prefix kernel (the dominant one) against the bf16 MFMA peak,
-               timed with HIP events on the stream it runs on
+  roofline     the split kernel (the dominant one) against the roofline that
+               binds the workload (bf16 MFMA or HBM), timed with HIP events on
+               the stream it runs on; traffic from committed counter passes
   cpu_baseline the fp64 oracle on host cores, same workload (test infrastructure)
 Details go to stderr.
 
-  python bench.py [--steps K] [--warmup W] [--config 1..7] [--no-cpu]
-                  [--slot-mode scrambled|contiguous|churned]
+  python bench.py [--steps K] [--warmup W] [--warm-seconds S] [--config 1..7]
+                  [--prefix L] [--chunk C] [--slot-mode MODE] [--launch eager|graph]
+                  [--device-lengths] [--defrag] [--std-q SD] [--gemm-ref] [--no-cpu]
 
 Besides the mean over the K timed steps, stderr and `config` carry per-step
 percentiles (HIP events around each step), the same steps with one pool copy
-(KV warm in the Infinity Cache), and the effective KV rate as a fraction of a
-measured device-copy rate.
+(KV warm in the Infinity Cache), the effective KV rate as a fraction of a
+measured device-copy rate, the split pass's softmax restarts per call, the
+launches per step (one when every request fits one chunk), a plain read of
+the step's own KV rows (`kv_read_ceiling`) and, with --gemm-ref, the vendor
+library's GEMMs of the same two shapes.
 """
 
 from __future__ import annotations
