@@ -42,3 +42,6 @@ def test_static_workspace_matches_caller_workspace_twice():
     small = gen.make_inputs([700], [gen.random_tree(5, rng)], 4, 1024, "scrambled", seed=56)
     _both(big)
     _both(small)
+    # and a one-chunk plan, where the split pass writes the output itself
+    short = gen.make_inputs([40], [gen.random_tree(9, rng)], 16, 512, "scrambled", seed=57)
+    _both(short)
