@@ -93,3 +93,92 @@ def test_no_vgpr_spills(asm):
     scratch = [int(v) for v in re.findall(r"\.private_segment_fixed_size:\s+(\d+)", asm)]
     assert spills and max(spills) == 0
     assert scratch and max(scratch) == 0
+
+
+def _blocks(lines):
+    """Basic blocks of the kernel's assembly: (label or None, [(line number,
+    instruction, inside inline asm)], successor labels, falls through)."""
+    blocks, cur, label, in_asm = [], [], None, False
+
+    def close(succ, falls):
+        blocks.append((label, cur, succ, falls))
+
+    for i, raw in enumerate(lines):
+        s = raw.strip()
+        if s.startswith(";;#ASMSTART"):
+            in_asm = True
+            continue
+        if s.startswith(";;#ASMEND"):
+            in_asm = False
+            continue
+        m = re.match(r"^(\.LBB\w+):", s)
+        if m:
+            if cur or label is not None:
+                close([], True)
+            cur, label = [], m.group(1)
+            continue
+        if not s or s.startswith((";", ".")) or s.endswith(":"):
+            continue
+        cur.append((i, s, in_asm))
+        op = s.split()[0]
+        if op.startswith(("s_branch", "s_cbranch", "s_setpc", "s_endpgm")):
+            tgt = s.split()[1] if len(s.split()) > 1 and op != "s_endpgm" else None
+            close([tgt] if tgt and tgt.startswith(".LBB") else [], op.startswith("s_cbranch"))
+            cur, label = [], None
+    if cur:
+        close([], False)
+    return blocks
+
+
+def test_slot_loads_read_only_after_their_wait(asm):
+    """The PV waves load the slot indices of a tile ahead with an asm
+    `global_load_dword` and name the register in the asm `s_waitcnt vmcnt`
+    that ends the iteration.  A read of that register before a wait sees
+    stale data.  Over every path of the compiled kernel (a forward dataflow
+    over its basic blocks), the only read allowed before the wait is a move
+    directly in front of a `vmcnt(0)` wait: the path that waits for
+    everything is the one on which no gather follows in the item, so the
+    slot value is dead there; on the path that gathers again (`vmcnt(9)`)
+    the register must be read after the wait."""
+    blocks = _blocks(asm.splitlines())
+    index = {b[0]: k for k, b in enumerate(blocks) if b[0]}
+    succ = []
+    for k, (_, _, tg, falls) in enumerate(blocks):
+        nxt = [index[x] for x in tg if x in index]
+        if falls and k + 1 < len(blocks):
+            nxt.append(k + 1)
+        succ.append(nxt)
+    n_loads = sum(1 for b in blocks for _, s, a in b[1] if a and s.split()[0] == "global_load_dword")
+    entry = [frozenset() for _ in blocks]
+    bad = set()
+    work = list(range(len(blocks)))
+    while work:
+        k = work.pop()
+        pend = set(entry[k])
+        ins = blocks[k][1]
+        for j, (i, s, in_asm) in enumerate(ins):
+            op = s.split()[0]
+            if in_asm and op == "global_load_dword":
+                pend |= _regs(s.split()[1].rstrip(","))
+                continue
+            if op == "s_waitcnt" and "vmcnt" in s:
+                pend = set()
+                continue
+            if pend:
+                srcs = set()
+                for tok in s.split()[2:]:
+                    srcs |= _regs(tok.rstrip(","))
+                if srcs & pend:
+                    nxt = ins[j + 1][1] if j + 1 < len(ins) else ""
+                    if not (op.startswith("v_mov") and nxt.startswith("s_waitcnt") and "vmcnt(0)" in nxt):
+                        bad.add(f"line {i + 1}: {s} (next: {nxt or 'end of block'})")
+            if op.startswith("v_") and not op.startswith(("v_cmp", "v_cmpx")) and len(s.split()) > 1:
+                pend -= _regs(s.split()[1].rstrip(","))
+        out = frozenset(pend)
+        for n in succ[k]:
+            merged = entry[n] | out
+            if merged != entry[n]:
+                entry[n] = merged
+                work.append(n)
+    assert n_loads >= 1, "no asm slot load found"
+    assert not bad, "slot-load registers read before their wait:\n" + "\n".join(sorted(bad)[:10])
