@@ -97,7 +97,25 @@ def test_no_vgpr_spills(asm):
 
 def _blocks(lines):
     """Basic blocks of the kernel's assembly: (label or None, [(line number,
-    instruction, inside inline asm)], successor labels, falls through)."""
+    instruction, inside inline asm)], successor labels, falls through).
+    Numeric local labels inside inline asm (`1:`, branched to as `1f` /
+    `1b`) are given unique names."""
+    # name every numeric local label by its line, and resolve 1f / 1b
+    local = {}
+    for i, raw in enumerate(lines):
+        m = re.match(r"^\s*(\d+):\s*$", raw)
+        if m:
+            local.setdefault(m.group(1), []).append(i)
+
+    def resolve(tok, i):
+        m = re.match(r"^(\d+)([fb])$", tok)
+        if not m or m.group(1) not in local:
+            return tok
+        cands = local[m.group(1)]
+        j = min((c for c in cands if c > i), default=None) if m.group(2) == "f" else \
+            max((c for c in cands if c < i), default=None)
+        return f".L_local_{j}" if j is not None else tok
+
     blocks, cur, label, in_asm = [], [], None, False
 
     def close(succ, falls):
@@ -112,18 +130,19 @@ def _blocks(lines):
             in_asm = False
             continue
         m = re.match(r"^(\.LBB\w+):", s)
-        if m:
+        n = re.match(r"^(\d+):$", s)
+        if m or n:
             if cur or label is not None:
                 close([], True)
-            cur, label = [], m.group(1)
+            cur, label = [], (m.group(1) if m else f".L_local_{i}")
             continue
         if not s or s.startswith((";", ".")) or s.endswith(":"):
             continue
         cur.append((i, s, in_asm))
         op = s.split()[0]
         if op.startswith(("s_branch", "s_cbranch", "s_setpc", "s_endpgm")):
-            tgt = s.split()[1] if len(s.split()) > 1 and op != "s_endpgm" else None
-            close([tgt] if tgt and tgt.startswith(".LBB") else [], op.startswith("s_cbranch"))
+            tgt = resolve(s.split()[1], i) if len(s.split()) > 1 and op != "s_endpgm" else None
+            close([tgt] if tgt and tgt.startswith(".L") else [], op.startswith("s_cbranch"))
             cur, label = [], None
     if cur:
         close([], False)
