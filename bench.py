@@ -58,8 +58,8 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
 MEASURED_TRAFFIC = {
     # (sha256(prefix_splitkv.hip + kernels.h + vamla.cpp), workload):
     #     (fetch KiB, write KiB, fetch scale, write scale)
-    ("830f552dfca411f26fae6011d8ece9414548b041f2254fb9c7ed56e36140a02f", 3): (59320.6, 31260.9, 2.0, 1.0),
-    ("830f552dfca411f26fae6011d8ece9414548b041f2254fb9c7ed56e36140a02f", 6): (74238.9, 6572.8, 2.0, 1.0),
+    ("9617fbf8965df8a02c5779e0c04c0ab8af33d6b620392d9e357f313bf8a2731f", 3): (59483.7, 31260.9, 2.0, 1.0),
+    ("9617fbf8965df8a02c5779e0c04c0ab8af33d6b620392d9e357f313bf8a2731f", 6): (74241.5, 6572.8, 2.0, 1.0),
 }
 KERNEL_SOURCES = ("prefix_splitkv.hip", "kernels.h", "vamla.cpp")
 KV_ROW_BYTES = 576 * 2

@@ -338,6 +338,10 @@ __global__ __launch_bounds__(512, 1) void prefix_splitkv_kernel(PrefixArgs a) {
     for (int t = 0; t < 4; ++t) slot_first[t] = (uint32_t)*slot_ptr(t, w - 4);
   }
 
+  // A barrier with no wait: every wave reaches it with its loads issued, so
+  // the QK waves' Q loads (144 KB) queue behind the slot indices instead of
+  // ahead of them (the slots start the dependent slot -> row round trips).
+  __builtin_amdgcn_s_barrier();
   if (ntt > 0) {
     for (int i = threadIdx.x; i < n_tree; i += blockDim.x) sh.par[i] = a.parent[t0 + i];
     __syncthreads();
@@ -367,16 +371,23 @@ __global__ __launch_bounds__(512, 1) void prefix_splitkv_kernel(PrefixArgs a) {
     // their scores stay 0, so their P is finite and their rows are dropped
     const int live_pr = rows_b - tile * kRowTile - 32 * pr;
     const int nb_live = __builtin_amdgcn_readfirstlane(live_pr <= 0 ? 0 : live_pr <= 16 ? 1 : 2);
+    // Q of the live 16-row halves (a dead half is never multiplied, so it
+    // is not loaded: on a 16-row tile that is three quarters of the loads)
     bf16x8 qf[kQSteps][2];
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
       const int row = tile * kRowTile + 32 * pr + 16 * nb + l16;
       const bool ok = row < rows_b;
       const uint16_t* qrow = a.q + ((size_t)t0 * a.num_heads + (ok ? row : 0)) * kDqk;
+      if (nb < nb_live) {
 #pragma unroll
-      for (int st = 0; st < kQSteps; ++st) {
-        const bf16x8 v = *(const bf16x8*)(qrow + (4 * st + q4) * 8);
-        qf[st][nb] = ok ? v : bf16x8{};
+        for (int st = 0; st < kQSteps; ++st) {
+          const bf16x8 v = *(const bf16x8*)(qrow + (4 * st + q4) * 8);
+          qf[st][nb] = ok ? v : bf16x8{};
+        }
+      } else {
+#pragma unroll
+        for (int st = 0; st < kQSteps; ++st) qf[st][nb] = bf16x8{};
       }
     }
     // K fragment of step st: key 16hf + l16 = unit 2hf + (l16 >> 3), key
