@@ -52,6 +52,15 @@ def _regs(tok):
     return {int(m.group(1))} if m else set()
 
 
+def _function(asm, name):
+    """Lines of the kernel whose symbol contains `name`, from its label to
+    its end marker."""
+    lines = asm.splitlines()
+    start = next(i for i, l in enumerate(lines) if re.match(r"^_Z\S*" + name + r"\S*:", l))
+    end = next(i for i in range(start, len(lines)) if lines[i].startswith(".Lfunc_end"))
+    return lines[start:end]
+
+
 def _pv_loop(lines):
     """Line range of the PV waves' key loop: the innermost loop holding the
     32x32x16 MFMAs, from its header label to its back-edge branch."""
@@ -63,7 +72,7 @@ def _pv_loop(lines):
 
 
 def test_no_copies_of_lds_reads_in_flight(asm):
-    lines = asm.splitlines()
+    lines = _function(asm, "prefix_splitkv_kernel")
     a, b = _pv_loop(lines)
     inflight, bad, n_reads = set(), [], 0
     for i in range(a, b + 1):
@@ -149,6 +158,56 @@ def _blocks(lines):
     return blocks
 
 
+def _reads_before_wait(lines, is_load, clears, allowed):
+    """Forward dataflow over the basic blocks of `lines`: registers written by
+    an async load (is_load(op)) are pending until a wait (clears(s)); every
+    instruction that reads a pending register must satisfy allowed(op, next
+    instruction).  Returns (loads seen, violations)."""
+    blocks = _blocks(lines)
+    index = {b[0]: k for k, b in enumerate(blocks) if b[0]}
+    succ = []
+    for k, (_, _, tg, falls) in enumerate(blocks):
+        nxt = [index[x] for x in tg if x in index]
+        if falls and k + 1 < len(blocks):
+            nxt.append(k + 1)
+        succ.append(nxt)
+    n_loads = sum(1 for b in blocks for _, s, a in b[1] if a and is_load(s.split()[0]))
+    entry = [frozenset() for _ in blocks]
+    bad = set()
+    work = list(range(len(blocks)))
+    while work:
+        k = work.pop()
+        pend = set(entry[k])
+        ins = blocks[k][1]
+        for j, (i, s, in_asm) in enumerate(ins):
+            op = s.split()[0]
+            if in_asm and is_load(op):
+                pend |= _regs(s.split()[1].rstrip(","))
+                continue
+            if clears(s):
+                pend = set()
+                continue
+            if pend:
+                srcs = set()
+                for tok in s.split()[2:]:
+                    srcs |= _regs(tok.rstrip(","))
+                if op.startswith(("v_mfma", "v_smfmac")) and len(s.split()) > 2:
+                    srcs |= _regs(s.split()[1].rstrip(","))          # accumulator in/out
+                if srcs & pend:
+                    nxt = ins[j + 1][1] if j + 1 < len(ins) else ""
+                    if not allowed(op, nxt):
+                        bad.add(f"line {i + 1}: {s} (next: {nxt or 'end of block'})")
+            if op.startswith("v_") and not op.startswith(("v_cmp", "v_cmpx", "v_mfma")) and len(s.split()) > 1:
+                pend -= _regs(s.split()[1].rstrip(","))
+        out = frozenset(pend)
+        for n in succ[k]:
+            merged = entry[n] | out
+            if merged != entry[n]:
+                entry[n] = merged
+                work.append(n)
+    return n_loads, sorted(bad)
+
+
 def test_slot_loads_read_only_after_their_wait(asm):
     """The PV waves load the slot indices of a tile ahead with an asm
     `global_load_dword` and name the register in the asm `s_waitcnt vmcnt`
@@ -159,45 +218,10 @@ def test_slot_loads_read_only_after_their_wait(asm):
     everything is the one on which no gather follows in the item, so the
     slot value is dead there; on the path that gathers again (`vmcnt(9)`)
     the register must be read after the wait."""
-    blocks = _blocks(asm.splitlines())
-    index = {b[0]: k for k, b in enumerate(blocks) if b[0]}
-    succ = []
-    for k, (_, _, tg, falls) in enumerate(blocks):
-        nxt = [index[x] for x in tg if x in index]
-        if falls and k + 1 < len(blocks):
-            nxt.append(k + 1)
-        succ.append(nxt)
-    n_loads = sum(1 for b in blocks for _, s, a in b[1] if a and s.split()[0] == "global_load_dword")
-    entry = [frozenset() for _ in blocks]
-    bad = set()
-    work = list(range(len(blocks)))
-    while work:
-        k = work.pop()
-        pend = set(entry[k])
-        ins = blocks[k][1]
-        for j, (i, s, in_asm) in enumerate(ins):
-            op = s.split()[0]
-            if in_asm and op == "global_load_dword":
-                pend |= _regs(s.split()[1].rstrip(","))
-                continue
-            if op == "s_waitcnt" and "vmcnt" in s:
-                pend = set()
-                continue
-            if pend:
-                srcs = set()
-                for tok in s.split()[2:]:
-                    srcs |= _regs(tok.rstrip(","))
-                if srcs & pend:
-                    nxt = ins[j + 1][1] if j + 1 < len(ins) else ""
-                    if not (op.startswith("v_mov") and nxt.startswith("s_waitcnt") and "vmcnt(0)" in nxt):
-                        bad.add(f"line {i + 1}: {s} (next: {nxt or 'end of block'})")
-            if op.startswith("v_") and not op.startswith(("v_cmp", "v_cmpx")) and len(s.split()) > 1:
-                pend -= _regs(s.split()[1].rstrip(","))
-        out = frozenset(pend)
-        for n in succ[k]:
-            merged = entry[n] | out
-            if merged != entry[n]:
-                entry[n] = merged
-                work.append(n)
+    n_loads, bad = _reads_before_wait(
+        _function(asm, "prefix_splitkv_kernel"),
+        is_load=lambda op: op == "global_load_dword",
+        clears=lambda s: s.startswith("s_waitcnt") and "vmcnt" in s,
+        allowed=lambda op, nxt: op.startswith("v_mov") and nxt.startswith("s_waitcnt") and "vmcnt(0)" in nxt)
     assert n_loads >= 1, "no asm slot load found"
-    assert not bad, "slot-load registers read before their wait:\n" + "\n".join(sorted(bad)[:10])
+    assert not bad, "slot-load registers read before their wait:\n" + "\n".join(bad[:10])
