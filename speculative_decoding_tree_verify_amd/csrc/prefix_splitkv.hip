@@ -33,8 +33,9 @@
 // fragment as the registers free up, and gather tile t+2 once their first
 // four MFMAs are under way.  The restart vote of tile t-2 is read early and
 // tested just before the barrier.  A tile whose query rows end inside it
-// skips the MFMAs of its dead 16-row halves (QK; with no live row in a pair,
-// its K reads too) and of rows 32..63 (PV) when they hold no live row.
+// skips the Q loads and MFMAs of its dead 16-row halves (QK; with no live
+// row in a pair, its K reads too) and the MFMAs of rows 32..63 (PV) when
+// they hold no live row.
 // With the request lengths read on the device, the chunk size comes from
 // the longest prefix in cu_prefix (device_chunk) instead of the host plan.
 //
