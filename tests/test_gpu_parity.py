@@ -481,3 +481,40 @@ def test_rows_beyond_4gib_of_pool():
     assert_close_out(out.float().cpu().numpy().astype(np.float64), ro, "beyond 4 GiB")
     del pool
     torch.cuda.empty_cache()
+
+
+def _sweep_case(i):
+    """Seeded random shape i of the sweep: 1-5 requests, 1-128 heads, trees of
+    1-65 nodes (random, bounded-depth or chains), prefixes from empty to 2500
+    keys with ragged ends, an explicit or planned chunk, a query spread from
+    near-uniform softmax to ~14 nats, and any slot layout."""
+    rng = np.random.default_rng(9000 + i)
+    B = int(rng.integers(1, 6))
+    H = int(rng.choice([1, 2, 3, 5, 8, 16, 32, 128]))
+    n_max = 65 if H <= 16 else 9                       # keep the oracle's work small at 128 heads
+    parents = []
+    for _ in range(B):
+        n = int(rng.integers(1, n_max + 1))
+        kind = rng.integers(3)
+        if kind == 0:
+            parents.append(gen.random_tree(n, rng))
+        elif kind == 1:
+            parents.append(gen.bounded_tree(n, rng))
+        else:
+            parents.append(np.arange(-1, n - 1, dtype=np.int32))   # a chain
+    lens = [int(v) for v in rng.choice([0, 1, 31, 32, 33, 95, 400, 777, 1500, 2500], B)]
+    chunk = int(rng.choice([0, 0, 32, 64, 96, 224, 512]))
+    std_q = float(rng.choice([0.1, 3.0, 30.0]))
+    mode = str(rng.choice(["scrambled", "contiguous", "churned"]))
+    need = sum(lens) + sum(len(p) for p in parents)
+    pool = need + 257 if mode != "churned" else need + 20000   # churn allocates up to 16384 slots at once
+    x = gen.make_inputs(lens, parents, H, pool, mode, seed=9100 + i, std_q=std_q, churn_requests=200)
+    return x, chunk, f"sweep {i}: B={B} H={H} N={[len(p) for p in parents]} L={lens} chunk={chunk} std_q={std_q} {mode}"
+
+
+@pytest.mark.parametrize("i", range(48))
+def test_random_shape_sweep(i):
+    # every third case reads the request lengths on the device
+    x, chunk, what = _sweep_case(i)
+    flags = vb.FLAG_DEVICE_LENGTHS if i % 3 == 2 else 0
+    check(x, chunk=chunk, what=what, flags=flags)
