@@ -9,6 +9,7 @@ CPU fallback.
 
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 from dataclasses import dataclass
@@ -207,10 +208,40 @@ def _ptr(t) -> int:
     return t.data_ptr()
 
 
-def _stream(stream=None) -> int:
+def _device(*tensors):
+    """The one GPU that every given tensor (None entries skipped) is on: the
+    call runs with it as the current device, on its stream."""
+    devs = {t.device for t in tensors if t is not None}
+    if any(d.type != "cuda" for d in devs):
+        raise ValueError("tensor must be on the GPU")
+    if len(devs) != 1:
+        raise ValueError(f"tensors must all be on one GPU, got {sorted(str(d) for d in devs)}")
+    return next(iter(devs))
+
+
+def _stream(stream=None, device=None) -> int:
+    """The HIP stream to enqueue on: the given one (which must belong to
+    device), else the device's current stream (read as its raw handle when
+    torch offers that, which costs a tenth of building a Stream object)."""
     torch = _torch()
-    s = torch.cuda.current_stream() if stream is None else stream
-    return s.cuda_stream
+    if stream is None:
+        raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+        if raw is not None and device is not None:
+            return raw(device.index)
+        stream = torch.cuda.current_stream(device)
+    if device is not None and stream.device != device:
+        raise ValueError(f"stream is on {stream.device}, the tensors on {device}")
+    return stream.cuda_stream
+
+
+def _on(device):
+    """Context that makes device current for the call (the library's arch
+    check and static workspace are per device); nothing to do when it is
+    current already."""
+    torch = _torch()
+    if torch.cuda.current_device() == device.index:
+        return contextlib.nullcontext()
+    return torch.cuda.device(device)
 
 
 def _bits(t, what: str):
@@ -312,10 +343,13 @@ def verify_attn_mla(prob: Problem, q, kv_pool, prefix_slot_idx, tree_slot_idx, p
         lse = torch.empty((T, H), dtype=torch.float32, device=q.device)
     _check_outputs(prob, out, lse)
     ws = ws or Workspace(prob, q.device)
+    dev = _device(q, kv_pool, prefix_slot_idx if prob.total_prefix else None, tree_slot_idx, parent, cu_prefix,
+                  cu_tree, out, lse, ws.buf)
     p = _params(prob, cu_prefix, cu_tree, ws)
-    st = lib().verify_attn_mla(ctypes.byref(p), _ptr(_bits(q, "q")), _ptr(_bits(kv_pool, "kv_pool")),
-                               _ptr(prefix_slot_idx) if prob.total_prefix else None, _ptr(tree_slot_idx),
-                               _ptr(parent), _ptr(out), _ptr(lse), _stream(stream))
+    with _on(dev):
+        st = lib().verify_attn_mla(ctypes.byref(p), _ptr(_bits(q, "q")), _ptr(_bits(kv_pool, "kv_pool")),
+                                   _ptr(prefix_slot_idx) if prob.total_prefix else None, _ptr(tree_slot_idx),
+                                   _ptr(parent), _ptr(out), _ptr(lse), _stream(stream, dev))
     _check(st, "verify_attn_mla")
     return out, lse
 
@@ -333,10 +367,15 @@ def verify_attn_mla_static(prob: Problem, q, kv_pool, prefix_slot_idx, tree_slot
     if lse is None:
         lse = torch.empty((T, H), dtype=torch.float32, device=q.device)
     _check_outputs(prob, out, lse)
+    dev = _device(q, kv_pool, prefix_slot_idx if prob.total_prefix else None, tree_slot_idx, parent, cu_prefix,
+                  cu_tree, out, lse)
     p = prob.params(_ptr(cu_prefix), _ptr(cu_tree))
-    st = lib().verify_attn_mla_static(ctypes.byref(p), _ptr(_bits(q, "q")), _ptr(_bits(kv_pool, "kv_pool")),
-                                      _ptr(prefix_slot_idx) if prob.total_prefix else None, _ptr(tree_slot_idx),
-                                      _ptr(parent), _ptr(out), _ptr(lse), _stream(stream))
+    # the static workspace is per device: the call runs with dev current
+    with _on(dev):
+        st = lib().verify_attn_mla_static(ctypes.byref(p), _ptr(_bits(q, "q")), _ptr(_bits(kv_pool, "kv_pool")),
+                                          _ptr(prefix_slot_idx) if prob.total_prefix else None,
+                                          _ptr(tree_slot_idx), _ptr(parent), _ptr(out), _ptr(lse),
+                                          _stream(stream, dev))
     _check(st, "verify_attn_mla_static")
     return out, lse
 
@@ -345,17 +384,26 @@ def split_partials(prob: Problem, q, kv_pool, prefix_slot_idx, tree_slot_idx, pa
                    ws: Workspace, stream=None):
     """Stage 1: chunk partials into the workspace (the last chunk of each
     request also covers its tree keys)."""
+    torch = _torch()
     _check_inputs(prob, q, kv_pool, prefix_slot_idx, tree_slot_idx, parent, cu_prefix, cu_tree)
+    dev = _device(q, kv_pool, prefix_slot_idx if prob.total_prefix else None, tree_slot_idx, parent, cu_prefix,
+                  cu_tree, ws.buf)
     p = _params(prob, cu_prefix, cu_tree, ws)
-    _check(lib().vamla_split_partials(ctypes.byref(p), _ptr(_bits(q, "q")), _ptr(_bits(kv_pool, "kv_pool")),
-                                      _ptr(prefix_slot_idx) if prob.total_prefix else None, _ptr(tree_slot_idx),
-                                      _ptr(parent), _stream(stream)), "vamla_split_partials")
+    with _on(dev):
+        _check(lib().vamla_split_partials(ctypes.byref(p), _ptr(_bits(q, "q")), _ptr(_bits(kv_pool, "kv_pool")),
+                                          _ptr(prefix_slot_idx) if prob.total_prefix else None,
+                                          _ptr(tree_slot_idx), _ptr(parent), _stream(stream, dev)),
+               "vamla_split_partials")
 
 
 def lse_merge(prob: Problem, cu_prefix, cu_tree, ws: Workspace, out, lse, stream=None):
+    torch = _torch()
     _check_outputs(prob, out, lse)
+    dev = _device(cu_prefix, cu_tree, ws.buf, out, lse)
     p = _params(prob, cu_prefix, cu_tree, ws)
-    _check(lib().vamla_lse_merge(ctypes.byref(p), _ptr(out), _ptr(lse), _stream(stream)), "vamla_lse_merge")
+    with _on(dev):
+        _check(lib().vamla_lse_merge(ctypes.byref(p), _ptr(out), _ptr(lse), _stream(stream, dev)),
+               "vamla_lse_merge")
 
 
 def slot_gather(kv_pool, idx, dst=None, stream=None):
@@ -368,8 +416,10 @@ def slot_gather(kv_pool, idx, dst=None, stream=None):
     if dst is None:
         dst = torch.empty((n, D_QK), dtype=kv_pool.dtype, device=kv_pool.device)
     _shaped(dst, (n, D_QK), _bf16_like(), "dst")
-    _check(lib().vamla_slot_gather(_ptr(_bits(kv_pool, "kv_pool")), _ptr(idx) if n else None, n,
-                                   _ptr(dst) if n else None, _stream(stream)), "vamla_slot_gather")
+    dev = _device(kv_pool, idx, dst)
+    with _on(dev):
+        _check(lib().vamla_slot_gather(_ptr(_bits(kv_pool, "kv_pool")), _ptr(idx) if n else None, n,
+                                       _ptr(dst) if n else None, _stream(stream, dev)), "vamla_slot_gather")
     return dst
 
 
@@ -385,8 +435,10 @@ def read_rows(kv_pool, idx, sink=None, stream=None):
         sink = torch.empty(READ_ROWS_SINK_WORDS, dtype=torch.int32, device=kv_pool.device)
     _shaped(sink, (READ_ROWS_SINK_WORDS,), (torch.int32,), "sink")
     n = idx.numel()
-    _check(lib().vamla_read_rows(_ptr(_bits(kv_pool, "kv_pool")), _ptr(idx) if n else None, n, _ptr(sink),
-                                 _stream(stream)), "vamla_read_rows")
+    dev = _device(kv_pool, idx, sink)
+    with _on(dev):
+        _check(lib().vamla_read_rows(_ptr(_bits(kv_pool, "kv_pool")), _ptr(idx) if n else None, n, _ptr(sink),
+                                     _stream(stream, dev)), "vamla_read_rows")
     return sink
 
 

@@ -113,7 +113,54 @@ int64_t choose_chunk(const vamla_params* p, int64_t row_tiles, int64_t rows) {
   return best_c;
 }
 
+// The plan depends only on the scalar fields of the parameters, so a caller
+// that repeats one shape (a serving loop) gets it from a cache: one entry per
+// host thread, so concurrent callers never share it.
+struct PlanKey {
+  int32_t batch, num_heads, d_qk, d_v;
+  int64_t pool_slots;
+  float softmax_scale;
+  int32_t max_tree, total_tree;
+  int64_t max_prefix, total_prefix;
+  int32_t chunk;
+  uint32_t flags;
+};
+thread_local PlanKey t_plan_key;
+thread_local vamla_plan_info t_plan;
+thread_local bool t_plan_valid = false;
+
+int make_plan_uncached(const vamla_params* p, vamla_plan_info* out);
+
 int make_plan(const vamla_params* p, vamla_plan_info* out) {
+  if (!p) return VAMLA_ERR_INVALID_ARG;
+  PlanKey k;
+  std::memset(&k, 0, sizeof(k));   // padding included, for the byte compare
+  k.batch = p->batch;
+  k.num_heads = p->num_heads;
+  k.d_qk = p->d_qk;
+  k.d_v = p->d_v;
+  k.pool_slots = p->pool_slots;
+  k.softmax_scale = p->softmax_scale;
+  k.max_tree = p->max_tree;
+  k.total_tree = p->total_tree;
+  k.max_prefix = p->max_prefix;
+  k.total_prefix = p->total_prefix;
+  k.chunk = p->chunk;
+  k.flags = p->flags;
+  if (t_plan_valid && std::memcmp(&k, &t_plan_key, sizeof(k)) == 0) {
+    *out = t_plan;
+    return VAMLA_OK;
+  }
+  const int st = make_plan_uncached(p, out);
+  if (st == VAMLA_OK) {
+    t_plan_key = k;
+    t_plan = *out;
+    t_plan_valid = true;
+  }
+  return st;
+}
+
+int make_plan_uncached(const vamla_params* p, vamla_plan_info* out) {
   const int st = check_shape(p);
   if (st != VAMLA_OK) return st;
   vamla_plan_info pl;

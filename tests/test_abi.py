@@ -3,6 +3,7 @@ declares, and its host-only entry points (planning, workspace sizing,
 validation, argument checks) behave without touching a GPU."""
 
 import ctypes
+import dataclasses
 import math
 import os
 import re
@@ -341,6 +342,41 @@ def test_binding_checks_arguments_before_any_launch(L):
         vb.slot_gather(ok["kv_pool"], torch.zeros(4, dtype=torch.int64))
     with pytest.raises((TypeError, ValueError)):
         vb.slot_gather(ok["kv_pool"], torch.zeros(4, dtype=torch.int32), dst=torch.zeros((3, 576), dtype=torch.bfloat16))
+
+
+def test_plan_cache_follows_every_scalar(L):
+    # the library keeps the last plan per host thread, keyed by every scalar
+    # field: alternating problems must each get their own plan back
+    probs = [prob(1), prob(3), prob(6), prob(1)]
+    fresh = []
+    for p in probs:
+        info = vb.plan(p)
+        fresh.append((info.chunk, info.row_tiles, info.max_chunks, info.grid_items, info.workspace_bytes))
+    assert fresh[0] == fresh[3] and fresh[0] != fresh[1] and fresh[1] != fresh[2]
+    base = prob(3)
+    a = vb.plan(base)
+    changes = [dict(chunk=256), dict(num_heads=8), dict(max_tree=9, total_tree=9), dict(total_prefix=1000),
+               dict(max_prefix=70000), dict(flags=vb.FLAG_DEVICE_LENGTHS)]
+    for ch in changes:
+        b = vb.plan(dataclasses.replace(base, **ch))
+        again = vb.plan(base)
+        assert (again.chunk, again.max_chunks, again.workspace_bytes) == (a.chunk, a.max_chunks, a.workspace_bytes)
+        if "flags" not in ch:
+            assert (b.chunk, b.row_tiles, b.max_chunks) != (a.chunk, a.row_tiles, a.max_chunks), ch
+
+
+def test_binding_requires_one_device(L):
+    # every tensor of a call must be on one GPU: the call runs with that
+    # device current, on its stream (a tensor elsewhere would hand the
+    # kernels another device's pointers)
+    import types
+    import torch
+    on = lambda d: types.SimpleNamespace(device=torch.device(d))
+    assert vb._device(on("cuda:0"), None, on("cuda:0")) == torch.device("cuda:0")
+    with pytest.raises(ValueError, match="one GPU"):
+        vb._device(on("cuda:0"), on("cuda:1"))
+    with pytest.raises(ValueError, match="on the GPU"):
+        vb._device(on("cuda:0"), on("cpu"))
 
 
 def test_bench_refuses_more_than_one_gpu():
