@@ -58,9 +58,10 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
 MEASURED_TRAFFIC = {
     # (sha256(prefix_splitkv.hip + kernels.h + vamla.cpp), workload):
     #     (fetch KiB, write KiB, fetch scale, write scale); re-keyed without new
-    #     passes only after a comment-only edit whose compiled code was identical
-    ("c4bb8fda24e95a491c3ed05dfd2e151906db0c283fbe34f99f1bf48e512729f2", 3): (59483.7, 31260.9, 2.0, 1.0),
-    ("c4bb8fda24e95a491c3ed05dfd2e151906db0c283fbe34f99f1bf48e512729f2", 6): (74241.5, 6572.8, 2.0, 1.0),
+    #     passes only after edits that left the kernels' compiled code and every
+    #     plan identical (a comment; the host plan cache)
+    ("263dc7845971aa7537221fe9d92f42d6c7ee2ec7538c0a7b0348ef686c4efb59", 3): (59483.7, 31260.9, 2.0, 1.0),
+    ("263dc7845971aa7537221fe9d92f42d6c7ee2ec7538c0a7b0348ef686c4efb59", 6): (74241.5, 6572.8, 2.0, 1.0),
 }
 KERNEL_SOURCES = ("prefix_splitkv.hip", "kernels.h", "vamla.cpp")
 KV_ROW_BYTES = 576 * 2
