@@ -384,7 +384,6 @@ def split_partials(prob: Problem, q, kv_pool, prefix_slot_idx, tree_slot_idx, pa
                    ws: Workspace, stream=None):
     """Stage 1: chunk partials into the workspace (the last chunk of each
     request also covers its tree keys)."""
-    torch = _torch()
     _check_inputs(prob, q, kv_pool, prefix_slot_idx, tree_slot_idx, parent, cu_prefix, cu_tree)
     dev = _device(q, kv_pool, prefix_slot_idx if prob.total_prefix else None, tree_slot_idx, parent, cu_prefix,
                   cu_tree, ws.buf)
@@ -397,7 +396,6 @@ def split_partials(prob: Problem, q, kv_pool, prefix_slot_idx, tree_slot_idx, pa
 
 
 def lse_merge(prob: Problem, cu_prefix, cu_tree, ws: Workspace, out, lse, stream=None):
-    torch = _torch()
     _check_outputs(prob, out, lse)
     dev = _device(cu_prefix, cu_tree, ws.buf, out, lse)
     p = _params(prob, cu_prefix, cu_tree, ws)
