@@ -35,7 +35,9 @@
 // tested just before the barrier.  A tile whose query rows end inside it
 // skips the Q loads and MFMAs of its dead 16-row halves (QK; with no live
 // row in a pair, its K reads too) and the MFMAs of rows 32..63 (PV) when
-// they hold no live row.
+// they hold no live row.  A tile of more than 16 live rows brings its query
+// rows to the QK waves' registers through LDS: contiguous LDS-DMA into the
+// two ring slots the loop fills last, then fragment reads.
 // With the request lengths read on the device, the chunk size comes from
 // the longest prefix in cu_prefix (device_chunk) instead of the host plan.
 //
@@ -216,6 +218,22 @@ __device__ __forceinline__ void gather_tile(const uint8_t* pool_lane, uint32_t s
       : "memory");
 }
 
+// One LDS-DMA: lane l's 16 bytes at src go to LDS m + 16 l (m uniform).
+__device__ __forceinline__ void dma_1k(const void* src, uint32_t m) {
+  uint32_t saved;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0"
+               : "=&s"(saved)
+               : "v"(src), "s"(m)
+               : "memory");
+}
+
+// Query rows staged in LDS for the QK waves' registers: the 32 rows of a
+// pair (36 KB, contiguous in q) sit row-major, 72 pieces of 16 bytes a row,
+// piece p of row r at slot p ^ qswz(r).  The DMAs then copy contiguous
+// kilobytes of q, and the fragment reads (16 rows at one piece) hit 16
+// distinct bank quads: row r's quad is 8(r & 1) + the slot's low bits.
+__device__ __forceinline__ int qswz(int r) { return (r >> 1) & 7; }
+
 struct Shared {
   uint8_t pbuf[2][4][1024];                   // P operands, [parity][ks*2 + rb][lane*16]
   float2 mtl[3][4][64];                       // QK waves: per-lane max of each 16-row half, by tile mod 3
@@ -340,7 +358,7 @@ __global__ __launch_bounds__(512, 1) void prefix_splitkv_kernel(PrefixArgs a) {
   }
 
   // A barrier with no wait: every wave reaches it with its loads issued, so
-  // the QK waves' Q loads (144 KB) queue behind the slot indices instead of
+  // the QK waves' query DMAs (72 KB) queue behind the slot indices instead of
   // ahead of them (the slots start the dependent slot -> row round trips).
   __builtin_amdgcn_s_barrier();
   if (ntt > 0) {
@@ -365,6 +383,9 @@ __global__ __launch_bounds__(512, 1) void prefix_splitkv_kernel(PrefixArgs a) {
   //     hf = w & 1 (keys 16hf..16hf+15 of each tile).
   //   PV wave c = w - 4 (0..3): output columns [128c, 128c+128), all 64 rows.
   const size_t pidx = ((size_t)b * a.row_tiles + tile) * a.max_chunks + s;
+  // more than 16 live rows: the QK waves stage their query rows in LDS (one
+  // barrier more in both roles)
+  const bool stage_q = __builtin_amdgcn_readfirstlane(rows_b - tile * kRowTile > 16 ? 1 : 0) != 0;
   if (is_qk) {
     const int pr = w >> 1, hf = w & 1, q4 = lane >> 4, l16 = lane & 15;
     // 16-row halves of this pair that hold live query rows (0, 1 or 2): the
@@ -373,22 +394,64 @@ __global__ __launch_bounds__(512, 1) void prefix_splitkv_kernel(PrefixArgs a) {
     const int live_pr = rows_b - tile * kRowTile - 32 * pr;
     const int nb_live = __builtin_amdgcn_readfirstlane(live_pr <= 0 ? 0 : live_pr <= 16 ? 1 : 2);
     // Q of the live 16-row halves (a dead half is never multiplied, so it
-    // is not loaded: on a 16-row tile that is three quarters of the loads)
+    // is not loaded: on a 16-row tile that is three quarters of the loads).
+    // A tile with more than 16 live rows stages them in LDS first (ring
+    // slots 2 and 3, which the loop's first gathers refill only after the
+    // prologue barrier), as contiguous kilobytes of q by LDS-DMA, the two
+    // waves of a pair taking half of its rows each; after one more barrier
+    // each wave reads its fragments from there.  Whole kilobytes, each row
+    // copied once for both waves, take about a third of the time that the
+    // fragment-shaped global loads take.  A tile of at most 16 rows (one
+    // half in one pair) loads its fragments straight from q: there the tile
+    // gathers decide when the loop can start.
     bf16x8 qf[kQSteps][2];
+    if (stage_q) {
+      uint8_t* const qs = pr == 0 ? tile2 : tile3;
+      const int live_rows = min(max(live_pr, 0), 32);
+      const uint8_t* qpair =
+          (const uint8_t*)(a.q + ((size_t)t0 * a.num_heads + tile * kRowTile + 32 * pr) * kDqk);
+      const uint32_t m = lds_addr(qs);
+      const int nk = __builtin_amdgcn_readfirstlane((live_rows * kDqk * 2 + 1023) >> 10);
+      for (int j = 18 * hf; j < min(18 * hf + 18, nk); ++j) {
+        const int g = 64 * j + lane;                 // 16-byte slot of the pair's rows
+        const int r = g / kChunks16, sl = g - r * kChunks16;
+        const int rr = r < live_rows ? r : 0;        // dead rows: any live bytes (zeroed below)
+        dma_1k(qpair + (size_t)rr * (kDqk * 2) + ((sl ^ qswz(r)) << 4),
+               __builtin_amdgcn_readfirstlane(m + 1024 * j));
+      }
+      asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      const int row = tile * kRowTile + 32 * pr + 16 * nb + l16;
-      const bool ok = row < rows_b;
-      const uint16_t* qrow = a.q + ((size_t)t0 * a.num_heads + (ok ? row : 0)) * kDqk;
-      if (nb < nb_live) {
+      for (int nb = 0; nb < 2; ++nb) {
+        const int r = 16 * nb + l16;
+        const bool ok = r < live_rows;
+        const uint8_t* qrow = qs + r * (kDqk * 2);
+        if (nb < nb_live) {
 #pragma unroll
-        for (int st = 0; st < kQSteps; ++st) {
-          const bf16x8 v = *(const bf16x8*)(qrow + (4 * st + q4) * 8);
-          qf[st][nb] = ok ? v : bf16x8{};
+          for (int st = 0; st < kQSteps; ++st) {
+            const bf16x8 v = *(const bf16x8*)(qrow + (((4 * st + q4) ^ qswz(r)) << 4));
+            qf[st][nb] = ok ? v : bf16x8{};
+          }
+        } else {
+#pragma unroll
+          for (int st = 0; st < kQSteps; ++st) qf[st][nb] = bf16x8{};
         }
-      } else {
+      }
+    } else {
 #pragma unroll
-        for (int st = 0; st < kQSteps; ++st) qf[st][nb] = bf16x8{};
+      for (int nb = 0; nb < 2; ++nb) {
+        const int row = tile * kRowTile + 32 * pr + 16 * nb + l16;
+        const bool ok = row < rows_b;
+        const uint16_t* qrow = a.q + ((size_t)t0 * a.num_heads + (ok ? row : 0)) * kDqk;
+        if (nb < nb_live) {
+#pragma unroll
+          for (int st = 0; st < kQSteps; ++st) {
+            const bf16x8 v = *(const bf16x8*)(qrow + (4 * st + q4) * 8);
+            qf[st][nb] = ok ? v : bf16x8{};
+          }
+        } else {
+#pragma unroll
+          for (int st = 0; st < kQSteps; ++st) qf[st][nb] = bf16x8{};
+        }
       }
     }
     // K fragment of step st: key 16hf + l16 = unit 2hf + (l16 >> 3), key
@@ -590,20 +653,21 @@ __global__ __launch_bounds__(512, 1) void prefix_splitkv_kernel(PrefixArgs a) {
   const uint8_t* pool_lane = (const uint8_t*)a.pool + (((lane & 7) ^ swz(lane >> 3)) << 4);
   // slots of tile t; valid after the next vmcnt wait
   auto load_slot = [&](int t) -> uint32_t { return load_u32_async(slot_ptr(t, c)); };
-  for (;;) {
+  // tiles 0 and 1 are in flight while the QK waves stage their query rows
+  // (the barrier after which those rows have landed in ring slots 2 and 3);
+  // a restart gathers them again
+  gather_tile(pool_lane, slot_first[0], tile0, c);
+  if (ntiles > 1) gather_tile(pool_lane, slot_first[1], tile1, c);
+  if (stage_q) asm volatile("s_barrier" ::: "memory");
+  for (bool again = false;; again = true) {
     // Slot ring: svd holds the slots of tile it+2 (gathered in iteration it),
     // svn those of tile it+3.  Each iteration loads the next slots before its
     // gathers, so the in-order vector-memory counter never makes a slot load
     // wait for a gather.
-    uint32_t svd, svn;
-    {
-      const uint32_t s0 = slot_first[0], s1 = slot_first[1];
-      svd = slot_first[2];
-      svn = slot_first[3];
-      gather_tile(pool_lane, s0, tile0, c);
-      if (ntiles > 1) {
-        gather_tile(pool_lane, s1, tile1, c);
-      }
+    uint32_t svd = slot_first[2], svn = slot_first[3];
+    if (again) {
+      gather_tile(pool_lane, slot_first[0], tile0, c);
+      if (ntiles > 1) gather_tile(pool_lane, slot_first[1], tile1, c);
     }
     // tile 0 must have landed; tile 1's nine gathers may stay in flight
     // (iteration 0's closing wait covers them)
