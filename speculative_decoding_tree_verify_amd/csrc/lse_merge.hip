@@ -64,6 +64,10 @@ __device__ __forceinline__ State shfl_state(const State& x, int mask) {
 
 __global__ __launch_bounds__(64 * kWaves) void lse_merge_kernel(MergeArgs a) {
   __shared__ State red[kWaves][kRowTile];
+  // every kernel-argument load issued at once (see the split kernel: the
+  // compiler would otherwise load these only after the debug test's load)
+  asm volatile("" ::"s"(a.part_o), "s"(a.part_lse), "s"(a.cu_prefix), "s"(a.cu_tree), "s"(a.chunk_wave_bits),
+               "s"(a.device_lengths));
   if (a.debug_record && __builtin_amdgcn_readfirstlane(a.debug_record[0]) != 0) {
     // the index data failed the device-side check: every output is NaN (the
     // lengths may be what failed, so rows are covered by the call's totals)

@@ -255,6 +255,12 @@ __global__ __launch_bounds__(512, 1) void prefix_splitkv_kernel(PrefixArgs a) {
   static_assert(kRing == 4, "ring slots are picked by the low two bits of the tile index");
   auto ring = [&](int i) -> uint8_t* { i &= kRing - 1; return i == 0 ? tile0 : i == 1 ? tile1 : i == 2 ? tile2 : tile3; };
 
+  // The arguments that the item decode and the first loads need are named
+  // here, so that every kernel-argument load is issued at once: left to the
+  // compiler, those behind the debug test below wait for its loads, a second
+  // dependent round trip before the first slot index can be read.
+  asm volatile("" ::"s"(a.q), "s"(a.prefix_slot), "s"(a.tree_slot), "s"(a.cu_prefix), "s"(a.part_lse),
+               "s"(a.device_lengths), "s"(a.scale_log2));
   // with the debug flag, a failed device-side index check leaves no work;
   // when this pass writes the final output (one chunk per request), every
   // element of it is NaN instead, as the merge would make it
