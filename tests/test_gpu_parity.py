@@ -55,10 +55,14 @@ def test_several_row_tiles():
     check(x, chunk=256, what="3 row tiles")
 
 
-@pytest.mark.parametrize("H,N", [(1, 9), (2, 9), (5, 9), (7, 9), (16, 1)])
+@pytest.mark.parametrize("H,N", [(1, 9), (2, 9), (5, 9), (7, 9), (16, 1), (17, 1), (4, 8), (11, 3), (16, 3),
+                                 (7, 7), (8, 8), (9, 9)])
 def test_partly_live_row_tile(H, N):
-    # 9, 18, 45, 63 and 16 live rows in the only row tile: the MFMAs of dead
-    # 16-row halves (QK) and of dead rows 32..63 (PV) are skipped
+    # 9, 18, 45, 63, 16, 17, 32, 33, 48, 49 and 64 live rows in the only row
+    # tile, and 64 + 17 in two: the MFMAs of dead 16-row halves (QK) and of
+    # dead rows 32..63 (PV) are skipped; tiles of more than 16 rows stage
+    # their query rows in LDS, copying only the kilobytes that hold live rows
+    # (a pair with 1, 16 or 17 live rows ends inside a kilobyte)
     rng = np.random.default_rng(40 + H)
     x = small([1500], [gen.random_tree(N, rng)], H, seed=41 + H, std_q=3.0)
     check(x, chunk=256, what=f"{H * N} live rows")

@@ -225,3 +225,71 @@ def test_slot_loads_read_only_after_their_wait(asm):
         allowed=lambda op, nxt: op.startswith("v_mov") and nxt.startswith("s_waitcnt") and "vmcnt(0)" in nxt)
     assert n_loads >= 1, "no asm slot load found"
     assert not bad, "slot-load registers read before their wait:\n" + "\n".join(bad[:10])
+
+
+def _asm_segments(lines):
+    """(first, last) line numbers of every inline-asm statement."""
+    segs, start = [], None
+    for i, raw in enumerate(lines):
+        s = raw.strip()
+        if s.startswith(";;#ASMSTART"):
+            start = i
+        elif s.startswith(";;#ASMEND") and start is not None:
+            segs.append((start, i))
+            start = None
+    return segs
+
+
+def _pending_at(lines, starts, clears, sinks):
+    """Forward dataflow over the basic blocks of `lines`: a flag is raised at
+    the line numbers in `starts`, dropped by an instruction with clears(s);
+    returns the instructions with sinks(s) that some path reaches with the
+    flag raised."""
+    blocks = _blocks(lines)
+    index = {b[0]: k for k, b in enumerate(blocks) if b[0]}
+    succ = []
+    for k, (_, _, tg, falls) in enumerate(blocks):
+        nxt = [index[x] for x in tg if x in index]
+        if falls and k + 1 < len(blocks):
+            nxt.append(k + 1)
+        succ.append(nxt)
+    entry = [False] * len(blocks)
+    seen = [False] * len(blocks)
+    bad = set()
+    work = list(range(len(blocks)))
+    while work:
+        k = work.pop()
+        flag = entry[k]
+        seen[k] = True
+        for i, s, _ in blocks[k][1]:
+            if i in starts:
+                flag = True
+            elif clears(s):
+                flag = False
+            elif flag and sinks(s):
+                bad.add(f"line {i + 1}: {s}")
+        for n in succ[k]:
+            if flag and not entry[n]:
+                entry[n] = True
+                work.append(n)
+    return sorted(bad)
+
+
+def test_staged_query_rows_land_before_the_barrier(asm):
+    """A row tile of more than 16 rows stages its query rows in ring slots 2
+    and 3 with single LDS-DMAs (one per inline-asm statement, unlike the
+    nine-DMA tile gathers), and the QK waves read them after the next
+    barrier.  Every path from such a DMA must wait for all vector memory
+    (`vmcnt(0)`) before it reaches a barrier, or a wave could read a row the
+    other wave of its pair has not yet copied."""
+    lines = _function(asm, "prefix_splitkv_kernel")
+    starts = set()
+    for a, b in _asm_segments(lines):
+        dmas = [i for i in range(a, b + 1) if lines[i].strip().startswith("global_load_lds_dwordx4")]
+        if len(dmas) == 1:
+            starts.add(dmas[0])
+    assert starts, "no single-DMA query staging found"
+    bad = _pending_at(lines, starts,
+                      clears=lambda s: s.startswith("s_waitcnt") and "vmcnt(0)" in s,
+                      sinks=lambda s: s.startswith("s_barrier"))
+    assert not bad, "barrier reached with query-row DMAs in flight:\n" + "\n".join(bad[:10])
