@@ -405,9 +405,10 @@ __global__ __launch_bounds__(512, 1) void prefix_splitkv_kernel(PrefixArgs a) {
     // slots 2 and 3, which the loop's first gathers refill only after the
     // prologue barrier), as contiguous kilobytes of q by LDS-DMA, the two
     // waves of a pair taking half of its rows each; after one more barrier
-    // each wave reads its fragments from there.  Whole kilobytes, each row
-    // copied once for both waves, take about a third of the time that the
-    // fragment-shaped global loads take.  A tile of at most 16 rows (one
+    // each wave reads its fragments from there.  Each row is copied once
+    // for both waves, in whole kilobytes: fragment-shaped global loads of
+    // the same bytes (16 rows x 64 B per instruction) took twice as long,
+    // and loaded every row twice.  A tile of at most 16 rows (one
     // half in one pair) loads its fragments straight from q: there the tile
     // gathers decide when the loop can start.
     bf16x8 qf[kQSteps][2];
