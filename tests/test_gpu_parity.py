@@ -218,7 +218,9 @@ def test_repeated_restarts_leave_other_rows_exact():
     # restarts of the chunk.  Every other row of the tile
     # (same row pair included) keeps a reference at or below its own max plus
     # the fixed margin, so all rows still match the oracle, and the climbing
-    # row ends on the last key
+    # row ends on the last key.  The tile's 36 rows are staged in LDS by the
+    # prologue; a restart keeps them in registers (their ring slots are
+    # refilled by then)
     rng = np.random.default_rng(70)
     H, N, node, head = 4, 9, 3, 2
     x = small([2000], [gen.random_tree(N, rng)], H, seed=71)
