@@ -363,9 +363,12 @@ __global__ __launch_bounds__(512, 1) void prefix_splitkv_kernel(PrefixArgs a) {
     for (int t = 0; t < 4; ++t) slot_first[t] = (uint32_t)*slot_ptr(t, w - 4);
   }
 
-  // A barrier with no wait: every wave reaches it with its loads issued, so
-  // the QK waves' query DMAs (72 KB) queue behind the slot indices instead of
-  // ahead of them (the slots start the dependent slot -> row round trips).
+  // A barrier with no explicit wait: every wave reaches it with its loads
+  // issued, so the QK waves' query loads queue behind the slot indices
+  // instead of ahead of them (the slots start the dependent slot -> row round
+  // trips).  The compiler forms the PV waves' row addresses from the slot
+  // values before it, so in practice they reach it once the slots have
+  // returned (a cache hit: the index arrays are the same every step).
   __builtin_amdgcn_s_barrier();
   if (ntt > 0) {
     for (int i = threadIdx.x; i < n_tree; i += blockDim.x) sh.par[i] = a.parent[t0 + i];
